@@ -1,0 +1,33 @@
+"""CPU oracle for the Mesh-Attention tile hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and
+its Python binding) may import, call or link anything in this package; only
+the test-suite, the smoke check and the benchmark's CPU-baseline leg use it.
+
+The oracle is written from the definitions on the pages, in float64 numpy,
+with no blocking, no online softmax and no fusion:
+
+* ``block_list_ref``  - which (Q partition, KV partition) blocks one GPU of an
+  R x C mesh owns, in KV-partition-rotation order, and each block's causal
+  class (full / diagonal / skipped), found by brute force over token positions.
+* ``attention_ref`` / ``tile_rows_ref`` - exact two-pass softmax attention of
+  query rows over an arbitrary set of keys, returning the output and the
+  natural-log log-sum-exp of the scaled scores.
+* ``lse_merge_ref``  - the log-sum-exp weighted combination of partial
+  (output, lse) pairs.
+
+Every function here is pinned by CPU tests to something other than itself
+(library routines, closed forms, invariants, brute force); see the test files
+named ``test_oracle_*.py``.
+"""
+
+from .block_list import FULL, DIAG, SKIP, block_list_ref, mesh_tile_sets_ref
+from .attention import attention_ref, tile_rows_ref, tile_positions_ref
+from .merge import lse_merge_ref
+
+__all__ = [
+    "FULL", "DIAG", "SKIP",
+    "block_list_ref", "mesh_tile_sets_ref",
+    "attention_ref", "tile_rows_ref", "tile_positions_ref",
+    "lse_merge_ref",
+]

@@ -1,0 +1,227 @@
+"""Benchmark of the Mesh-Attention tile hot path on one MI355X.
+
+A step is one pass of the whole hot path over one synthetic tile: the host
+block list (tile geometry, KV-rotation order, causal classes), the tile
+forward (QK^T, mask, online softmax, PV, epilogue) and the LSE merge of the
+partial results of the query rows.  Inputs are resident in HBM before the
+timed region; the partial results that the mesh-row peers would return are
+produced once, untimed, by the same kernel on the sibling tiles.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5] [--no-cpu-baseline]
+
+Prints one JSON line on stdout (everything else goes to stderr).
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tile-forward TFLOP/s (% bf16 MFMA peak) + LSE-merge GB/s, 1M-token tile"
+PEAK_BF16_TFLOPS = 2516.6   # 4096 flop/clk/CU x 256 CUs x 2.4 GHz, dense
+PEAK_F32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def tile_flops(blocks, part_len, heads_q, head_dim):
+    """Algorithmic flops: 4*d per visible (query, key) pair per query head;
+    FULL blocks L*L pairs, DIAG blocks L*(L+1)/2, SKIP none."""
+    pairs = 0
+    for b in blocks:
+        if b[4] == 0:
+            pairs += part_len * part_len
+        elif b[4] == 1:
+            pairs += part_len * (part_len + 1) // 2
+    return 4.0 * head_dim * heads_q * pairs
+
+
+def merge_bytes(n, rows, d, elt):
+    """Algorithmic bytes of one merge: read n partial rows (O and lse), write one."""
+    return n * rows * (d * elt + 4) + rows * (d * elt + 4)
+
+
+def cpu_baseline(w, q, k, v, q_parts, kv_parts, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of query rows of the tile."""
+    import numpy as np
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    scale = 1.0 / math.sqrt(w.head_dim)
+    qh = q.detach().cpu().double().numpy()
+    kh = k.detach().cpu().double().numpy()
+    vh = v.detach().cpu().double().numpy()
+    qpos = oracle.tile_positions_ref(q_parts, w.part_len)
+    kpos = oracle.tile_positions_ref(kv_parts, w.part_len)
+    rows_all = workloads.sample_rows(q.shape[0], w.heads_q, w.heads_kv, w.part_len,
+                                     n_sample=200000, seed=3)
+    rng = np.random.default_rng(7)
+    rows_all = rows_all[rng.permutation(len(rows_all))]
+    done, flops, t_used, batch = 0, 0.0, 0.0, 16
+    while t_used < budget_s and done < len(rows_all):
+        rows = rows_all[done:done + batch]
+        t0 = time.perf_counter()
+        oracle.attention_ref(qh, kh, vh, qpos, kpos, w.causal, scale, rows=rows)
+        dt = time.perf_counter() - t0
+        vis = (kpos[None, :] <= qpos[rows[:, 0]][:, None]).sum(axis=1) if w.causal else \
+            np.full(len(rows), len(kpos))
+        flops += float(4.0 * w.head_dim * vis.sum())
+        t_used += dt
+        done += len(rows)
+        batch = min(4 * batch, max(16, int(len(rows) * (budget_s - t_used) / max(dt, 1e-3))))
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} (token, head) rows of the same tile, exact float64 two-pass "
+                      f"softmax over their visible keys, {t_used:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's tile only: the hot path is one GPU's share of the "
+              "mesh and this build has no multi-GPU path; run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import long_context_distributed_amd as mat
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = workloads.WORKLOADS[a.workload]
+    scale = 1.0 / math.sqrt(w.head_dim)
+    R, C, r, c = w.mesh_rows, w.mesh_cols, w.tile_row, w.tile_col
+
+    blocks = mat.block_list(R, C, r, c, w.causal, w.kv_rotate)
+    q_parts = [b[2] for b in blocks if b[1] == 0]
+    kv_parts = [b[3] for b in blocks if b[0] == 0]
+    log(f"[bench] workload {a.workload}: {w.name}")
+    q = workloads.gather(w, "q", q_parts, dev)
+    k = workloads.gather(w, "k", kv_parts, dev)
+    v = workloads.gather(w, "v", kv_parts, dev)
+    n_tok, d = q.shape[0], w.head_dim
+    rows = n_tok * w.heads_q
+    elt = 2 if w.dtype == "bf16" else 4
+
+    # Partial results the peers would return, produced once by the same kernel.
+    if w.merge == "per_kv_part":
+        n_parts, own = R, None
+    else:
+        n_parts, own = C, c
+    o_parts = torch.empty((n_parts, rows, d), dtype=q.dtype, device=dev)
+    l_parts = torch.empty((n_parts, rows), dtype=torch.float32, device=dev)
+    for i in range(n_parts):
+        if w.merge == "per_kv_part":
+            sub = [b for b in blocks if b[1] == i]
+            mat.tile_fwd(q, k, v, sub, w.part_len, scale, out=o_parts[i].view_as(q),
+                         lse=l_parts[i].view(n_tok, w.heads_q))
+        elif i != own:
+            sb = mat.block_list(R, C, r, i, w.causal, w.kv_rotate)
+            skv = [b[3] for b in sb if b[0] == 0]
+            ks = workloads.gather(w, "k", skv, dev)
+            vs = workloads.gather(w, "v", skv, dev)
+            mat.tile_fwd(q, ks, vs, sb, w.part_len, scale, out=o_parts[i].view_as(q),
+                         lse=l_parts[i].view(n_tok, w.heads_q))
+            del ks, vs
+    torch.cuda.synchronize()
+    if own is not None:
+        o_own, l_own = o_parts[own].view_as(q), l_parts[own].view(n_tok, w.heads_q)
+    else:
+        o_own = torch.empty_like(q)
+        l_own = torch.empty((n_tok, w.heads_q), dtype=torch.float32, device=dev)
+    o_m = torch.empty((rows, d), dtype=q.dtype, device=dev)
+    l_m = torch.empty((rows,), dtype=torch.float32, device=dev)
+
+    flops = tile_flops(blocks, w.part_len, w.heads_q, d)
+    mbytes = merge_bytes(n_parts, rows, d, elt)
+
+    ev = []
+
+    def step(record):
+        bl = mat.block_list(R, C, r, c, w.causal, w.kv_rotate)
+        e0 = torch.cuda.Event(enable_timing=True) if record else None
+        e1 = torch.cuda.Event(enable_timing=True) if record else None
+        e2 = torch.cuda.Event(enable_timing=True) if record else None
+        if record:
+            e0.record()
+        mat.tile_fwd(q, k, v, bl, w.part_len, scale, out=o_own, lse=l_own)
+        if record:
+            e1.record()
+        mat.lse_merge(o_parts, l_parts, out=o_m, lse_out=l_m)
+        if record:
+            e2.record()
+            ev.append((e0, e1, e2))
+
+    for _ in range(a.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = 1e3 * elapsed / a.steps
+    t_tile = sum(e0.elapsed_time(e1) for e0, e1, _ in ev) / len(ev)   # ms
+    t_merge = sum(e1.elapsed_time(e2) for _, e1, e2 in ev) / len(ev)  # ms
+    tile_tflops = flops / (t_tile * 1e-3) / 1e12
+    merge_gbs = mbytes / (t_merge * 1e-3) / 1e9
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    log(f"[bench] tile {t_tile:.3f} ms = {tile_tflops:.1f} TFLOP/s ({100 * tile_tflops / peak:.1f}% "
+        f"of {peak}); merge {t_merge:.3f} ms = {merge_gbs:.0f} GB/s "
+        f"({100 * merge_gbs / PEAK_HBM_GBS:.1f}% of HBM); step {ms_step:.3f} ms")
+
+    result = {
+        "metric": METRIC,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "mesh": f"{R}x{C}", "tile": [r, c],
+                   "part_len": w.part_len, "q_tokens": n_tok, "kv_tokens": k.shape[0],
+                   "heads_q": w.heads_q, "heads_kv": w.heads_kv, "head_dim": d,
+                   "causal": w.causal, "kv_rotate": w.kv_rotate, "merge_partials": n_parts,
+                   "parallelism": "one GPU's tile"},
+        "tile_fwd": {"ms": t_tile, "tflops": tile_tflops, "frac_peak": tile_tflops / peak,
+                     "flops": flops},
+        "lse_merge": {"ms": t_merge, "gbs": merge_gbs, "frac_hbm": merge_gbs / PEAK_HBM_GBS,
+                      "bytes": mbytes},
+        "roofline": {"bound": "mfma", "achieved": tile_tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": tile_tflops / peak, "traffic": None,
+                     "kernel": "tile_fwd_bf16_d128" if w.dtype == "bf16" else "tile_fwd_f32"},
+    }
+    if not a.no_cpu_baseline:
+        log("[bench] timing the oracle on host cores")
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, q_parts, kv_parts, a.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,140 @@
+"""Mesh-Attention tile hot path for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libmeshattn.so`` (include/mesh_attn.h):
+argument marshalling only.  PyTorch supplies device memory and the stream;
+every step of the computation runs in the library's HIP kernels.
+
+    block_list(mesh_rows, mesh_cols, row, col, causal, kv_rotate) -> [Block tuples]
+    tile_fwd(q, k, v, blocks, part_len, softmax_scale=None) -> (o, lse)
+    lse_merge(o_parts, lse_parts) -> (o, lse)
+"""
+import ctypes
+import math
+
+from . import _lib
+from ._lib import BF16, DIAG, F32, FULL, SKIP  # noqa: F401
+
+__all__ = ["MeshAttnError", "block_list", "tile_fwd", "lse_merge", "FULL", "DIAG", "SKIP",
+           "library_path"]
+
+
+class MeshAttnError(RuntimeError):
+    """A library call returned a non-zero status."""
+
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def library_path():
+    return _lib.LIB_PATH
+
+
+def _check(lib, status):
+    if status != _lib.OK:
+        msg = lib.mesh_attn_last_error().decode() or lib.mesh_attn_status_string(status).decode()
+        raise MeshAttnError(status, msg)
+
+
+def block_list(mesh_rows, mesh_cols, row, col, causal, kv_rotate):
+    """Blocks (q_slot, kv_slot, q_part, kv_part, kind) of tile (row, col)."""
+    lib = _lib.load()
+    n = ctypes.c_int32(0)
+    st = lib.mesh_attn_block_list(mesh_rows, mesh_cols, row, col, int(bool(causal)),
+                                  int(bool(kv_rotate)), None, 0, ctypes.byref(n))
+    if st != _lib.ERR_CAPACITY:
+        _check(lib, st)
+    arr = (_lib.Block * n.value)()
+    _check(lib, lib.mesh_attn_block_list(mesh_rows, mesh_cols, row, col, int(bool(causal)),
+                                         int(bool(kv_rotate)), arr, n.value, ctypes.byref(n)))
+    return [(b.q_slot, b.kv_slot, b.q_part, b.kv_part, b.kind) for b in arr]
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return _lib.BF16
+    if t.dtype == torch.float32:
+        return _lib.F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream_handle(stream, device):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _require_device(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a HIP device (no CPU path)")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def tile_fwd(q, k, v, blocks, part_len, softmax_scale=None, out=None, lse=None, stream=None):
+    """Forward of one tile.
+
+    q: [n_q_slots*L, H_q, d], k/v: [n_kv_slots*L, H_kv, d] on the device
+    (bf16 or f32, same dtype); blocks: iterable of (q_slot, kv_slot, q_part,
+    kv_part, kind).  Returns (o [n_q_slots*L, H_q, d], lse [n_q_slots*L, H_q]
+    float32), allocated with torch unless given.
+    """
+    import torch
+    lib = _lib.load()
+    _require_device(q, k, v)
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("expected q [Tq, Hq, d] and k, v [Tk, Hkv, d]")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k and v must share a dtype")
+    tq, hq, d = q.shape
+    tk, hkv, dk = k.shape
+    if dk != d:
+        raise ValueError("head_dim of q and k differ")
+    if tq % part_len or tk % part_len:
+        raise ValueError("token counts must be multiples of part_len")
+    blocks = list(blocks)
+    arr = (_lib.Block * max(1, len(blocks)))()
+    for i, b in enumerate(blocks):
+        arr[i] = _lib.Block(*[int(x) for x in b])
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    desc = _lib.TileDesc(_dtype_code(q), part_len, tq // part_len, tk // part_len, hq, hkv, d,
+                         scale, arr, len(blocks))
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
+    _require_device(out, lse)
+    if out.shape != q.shape or out.dtype != q.dtype or lse.shape != (tq, hq) or \
+            lse.dtype != torch.float32:
+        raise ValueError("output buffers have the wrong shape or dtype")
+    _check(lib, lib.mesh_attn_tile_fwd(ctypes.byref(desc), q.data_ptr(), k.data_ptr(),
+                                       v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                       _stream_handle(stream, q.device)))
+    return out, lse
+
+
+def lse_merge(o_parts, lse_parts, out=None, lse_out=None, want_lse=True, stream=None):
+    """Merge n partial results: o_parts [n, rows, d] (bf16/f32), lse_parts
+    [n, rows] float32 -> (o [rows, d], lse [rows] or None)."""
+    import torch
+    lib = _lib.load()
+    _require_device(o_parts, lse_parts)
+    if o_parts.dim() != 3 or lse_parts.shape != o_parts.shape[:2]:
+        raise ValueError("expected o_parts [n, rows, d] and lse_parts [n, rows]")
+    if lse_parts.dtype != torch.float32:
+        raise ValueError("lse_parts must be float32")
+    n, rows, d = o_parts.shape
+    if out is None:
+        out = torch.empty((rows, d), dtype=o_parts.dtype, device=o_parts.device)
+    if want_lse and lse_out is None:
+        lse_out = torch.empty((rows,), dtype=torch.float32, device=o_parts.device)
+    _require_device(out)
+    if out.shape != (rows, d) or out.dtype != o_parts.dtype:
+        raise ValueError("output buffer has the wrong shape or dtype")
+    _check(lib, lib.mesh_attn_lse_merge(n, rows, d, _dtype_code(o_parts), o_parts.data_ptr(),
+                                        lse_parts.data_ptr(), out.data_ptr(),
+                                        lse_out.data_ptr() if lse_out is not None else None,
+                                        _stream_handle(stream, o_parts.device)))
+    return out, lse_out

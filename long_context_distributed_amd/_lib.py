@@ -1,0 +1,78 @@
+"""ctypes declarations of the C ABI in include/mesh_attn.h.
+
+Loading the library needs only the HIP runtime shared library, not a GPU.
+There is no fallback: if libmeshattn.so has not been built, loading fails
+with an error that says how to build it.
+"""
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmeshattn.so")
+
+OK = 0
+ERR_INVALID = -1
+ERR_CAPACITY = -2
+ERR_UNSUPPORTED = -3
+ERR_HIP = -4
+
+BF16 = 0
+F32 = 1
+
+FULL = 0
+DIAG = 1
+SKIP = 2
+
+MAX_Q_SLOTS = 64
+MAX_KV_SLOTS = 64
+MAX_BLOCKS = 1024
+
+# Every symbol include/mesh_attn.h declares.
+EXPORTS = ("mesh_attn_block_list", "mesh_attn_tile_fwd", "mesh_attn_lse_merge",
+           "mesh_attn_status_string", "mesh_attn_last_error", "mesh_attn_version")
+
+
+class Block(ctypes.Structure):
+    _fields_ = [("q_slot", ctypes.c_int32), ("kv_slot", ctypes.c_int32),
+                ("q_part", ctypes.c_int32), ("kv_part", ctypes.c_int32),
+                ("kind", ctypes.c_int32)]
+
+
+class TileDesc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("part_len", ctypes.c_int32),
+                ("n_q_slots", ctypes.c_int32), ("n_kv_slots", ctypes.c_int32),
+                ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("blocks", ctypes.POINTER(Block)), ("n_blocks", ctypes.c_int32)]
+
+
+_LIB = None
+
+
+def load():
+    """The loaded library (cached).  Raises RuntimeError if it is not built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m long_context_distributed_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    fp = ctypes.POINTER(ctypes.c_float)
+    lib.mesh_attn_block_list.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(Block), i32,
+                                         ctypes.POINTER(i32)]
+    lib.mesh_attn_block_list.restype = ctypes.c_int
+    lib.mesh_attn_tile_fwd.argtypes = [ctypes.POINTER(TileDesc), vp, vp, vp, vp, vp, vp]
+    lib.mesh_attn_tile_fwd.restype = ctypes.c_int
+    lib.mesh_attn_lse_merge.argtypes = [i32, i64, i32, i32, vp, vp, vp, vp, vp]
+    lib.mesh_attn_lse_merge.restype = ctypes.c_int
+    lib.mesh_attn_status_string.argtypes = [ctypes.c_int]
+    lib.mesh_attn_status_string.restype = ctypes.c_char_p
+    lib.mesh_attn_last_error.argtypes = []
+    lib.mesh_attn_last_error.restype = ctypes.c_char_p
+    lib.mesh_attn_version.argtypes = []
+    lib.mesh_attn_version.restype = i32
+    del fp
+    _LIB = lib
+    return lib

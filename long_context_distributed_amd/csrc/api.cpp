@@ -1,0 +1,226 @@
+// C-ABI entry points: host-side validation, packing of the tile schedule into
+// kernel arguments, and launches on the caller's stream.
+//
+// Every argument is checked before the first HIP call, so every error path
+// can be exercised on a machine without a GPU.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "mesh_attn.h"
+#include "kernels.h"
+#include "status.h"
+
+namespace mesh_attn {
+
+namespace {
+thread_local std::string g_last_error;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) {
+        clear_error();
+        return MESH_ATTN_OK;
+    }
+    g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+    return MESH_ATTN_ERR_HIP;
+}
+
+int gcd(int a, int b) {
+    while (b != 0) {
+        const int t = a % b;
+        a = b;
+        b = t;
+    }
+    return a;
+}
+}  // namespace
+
+int fail(int status, const char* msg) {
+    g_last_error = msg;
+    return status;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+// Checks a tile description and packs its schedule.  Returns a status; on
+// success p.sched and the per-slot fields of p are filled in.
+static int build_schedule(const mesh_attn_tile_desc& d, TileParams& p) {
+    const int nq = d.n_q_slots, nkv = d.n_kv_slots;
+    if (d.n_blocks < 0 || d.n_blocks > MESH_ATTN_MAX_BLOCKS)
+        return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: n_blocks out of range");
+    if (d.n_blocks > 0 && d.blocks == nullptr)
+        return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: blocks is NULL");
+
+    // kind of each (q_slot, kv_slot); -1 = not listed
+    int8_t kind[kMaxQSlots][kMaxKvSlots];
+    memset(kind, -1, sizeof(kind));
+    int32_t q_part_of[kMaxQSlots], kv_part_of[kMaxKvSlots];
+    for (int i = 0; i < kMaxQSlots; ++i) q_part_of[i] = -1;
+    for (int i = 0; i < kMaxKvSlots; ++i) kv_part_of[i] = -1;
+
+    for (int i = 0; i < d.n_blocks; ++i) {
+        const mesh_attn_block& b = d.blocks[i];
+        if (b.q_slot < 0 || b.q_slot >= nq || b.kv_slot < 0 || b.kv_slot >= nkv)
+            return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: block slot out of range");
+        if (b.q_part < 0 || b.kv_part < 0)
+            return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: negative partition id");
+        if (b.kind < MESH_ATTN_FULL || b.kind > MESH_ATTN_SKIP)
+            return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: block kind out of range");
+        if (kind[b.q_slot][b.kv_slot] != -1)
+            return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: duplicated (q_slot, kv_slot) block");
+        if (q_part_of[b.q_slot] != -1 && q_part_of[b.q_slot] != b.q_part)
+            return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: q_slot listed with two partitions");
+        if (kv_part_of[b.kv_slot] != -1 && kv_part_of[b.kv_slot] != b.kv_part)
+            return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: kv_slot listed with two partitions");
+        if (b.kind == MESH_ATTN_DIAG && b.q_part != b.kv_part)
+            return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: DIAG block with q_part != kv_part");
+        kind[b.q_slot][b.kv_slot] = static_cast<int8_t>(b.kind);
+        q_part_of[b.q_slot] = b.q_part;
+        kv_part_of[b.kv_slot] = b.kv_part;
+    }
+    for (int a = 0; a < nq; ++a)
+        for (int b = a + 1; b < nq; ++b)
+            if (q_part_of[a] != -1 && q_part_of[a] == q_part_of[b])
+                return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: two Q slots hold one partition");
+    for (int a = 0; a < nkv; ++a)
+        for (int b = a + 1; b < nkv; ++b)
+            if (kv_part_of[a] != -1 && kv_part_of[a] == kv_part_of[b])
+                return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: two KV slots hold one partition");
+
+    // Pack non-SKIP entries per Q slot in KV-slot order; weigh each Q slot.
+    int cost2[kMaxQSlots];  // 2 per FULL, 1 per DIAG
+    int off = 0;
+    for (int s = 0; s < nq; ++s) {
+        p.sched.blk_off[s] = static_cast<uint16_t>(off);
+        cost2[s] = 0;
+        for (int j = 0; j < nkv; ++j) {
+            const int kd = kind[s][j];
+            if (kd == MESH_ATTN_FULL || kd == MESH_ATTN_DIAG) {
+                p.sched.blk[off++] = static_cast<uint8_t>((j << 2) | kd);
+                cost2[s] += kd == MESH_ATTN_FULL ? 2 : 1;
+            }
+        }
+    }
+    p.sched.blk_off[nq] = static_cast<uint16_t>(off);
+    int order[kMaxQSlots];
+    for (int s = 0; s < nq; ++s) order[s] = s;
+    std::stable_sort(order, order + nq, [&](int a, int b) { return cost2[a] > cost2[b]; });
+    for (int s = 0; s < nq; ++s) p.sched.q_order[s] = static_cast<uint8_t>(order[s]);
+    return MESH_ATTN_OK;
+}
+
+}  // namespace mesh_attn
+
+using namespace mesh_attn;
+
+extern "C" int mesh_attn_tile_fwd(const mesh_attn_tile_desc* desc, const void* q, const void* k,
+                                  const void* v, void* o, float* lse, void* hip_stream) {
+    if (desc == nullptr) return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: desc is NULL");
+    const mesh_attn_tile_desc& d = *desc;
+    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr)
+        return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: NULL tensor pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: tensor pointer not 16-byte aligned");
+    if (d.dtype != MESH_ATTN_BF16 && d.dtype != MESH_ATTN_F32)
+        return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: unknown dtype");
+    if (d.part_len < 1) return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: part_len must be >= 1");
+    if (d.n_q_slots < 1 || d.n_q_slots > MESH_ATTN_MAX_Q_SLOTS)
+        return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: n_q_slots out of range");
+    if (d.n_kv_slots < 1 || d.n_kv_slots > MESH_ATTN_MAX_KV_SLOTS)
+        return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: n_kv_slots out of range");
+    if (d.heads_q < 1 || d.heads_kv < 1 || d.heads_q % d.heads_kv != 0)
+        return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: heads_q must be a positive multiple of heads_kv");
+    if (d.head_dim < 1) return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: head_dim must be >= 1");
+    if (!(isfinite(d.softmax_scale) && d.softmax_scale > 0.0f))
+        return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: softmax_scale must be finite and > 0");
+    // Element counts must stay addressable with 64-bit offsets and the token
+    // index with 32-bit integers.
+    const int64_t q_tokens = static_cast<int64_t>(d.n_q_slots) * d.part_len;
+    const int64_t kv_tokens = static_cast<int64_t>(d.n_kv_slots) * d.part_len;
+    if (q_tokens > INT32_MAX || kv_tokens > INT32_MAX ||
+        q_tokens * d.heads_q > INT32_MAX || kv_tokens * d.heads_kv > INT32_MAX)
+        return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: tile too large");
+    const bool supported = (d.dtype == MESH_ATTN_BF16 && d.head_dim == 128) ||
+                           (d.dtype == MESH_ATTN_F32 && (d.head_dim == 64 || d.head_dim == 128));
+    if (!supported)
+        return fail(MESH_ATTN_ERR_UNSUPPORTED, "tile_fwd: dtype/head_dim combination not built");
+
+    TileParams p;
+    memset(&p, 0, sizeof(p));
+    const int st = build_schedule(d, p);
+    if (st != MESH_ATTN_OK) return st;
+
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.part_len = d.part_len;
+    p.heads_q = d.heads_q;
+    p.heads_kv = d.heads_kv;
+    p.group = d.heads_q / d.heads_kv;
+    p.heads_per_wg = gcd(p.group, kTileWaves);
+    p.tok_groups = kTileWaves / p.heads_per_wg;
+    p.n_tok_blocks = (d.part_len + 32 * p.tok_groups - 1) / (32 * p.tok_groups);
+    p.n_head_groups = p.group / p.heads_per_wg;
+    p.n_q_slots = d.n_q_slots;
+    p.scale_log2e = d.softmax_scale * 1.4426950408889634f;
+
+    const int64_t n_wg = static_cast<int64_t>(d.n_q_slots) * p.n_tok_blocks * d.heads_kv *
+                         p.n_head_groups;
+    if (n_wg > INT32_MAX) return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: grid too large");
+
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    const hipError_t e = d.dtype == MESH_ATTN_BF16 ? launch_tile_fwd_bf16(p, d.head_dim, stream)
+                                                   : launch_tile_fwd_f32(p, d.head_dim, stream);
+    return hip_status(e, "tile_fwd: kernel launch failed");
+}
+
+extern "C" int mesh_attn_lse_merge(int32_t n_parts, int64_t rows, int32_t head_dim, int32_t dtype,
+                                   const void* o_parts, const float* lse_parts, void* o_out,
+                                   float* lse_out, void* hip_stream) {
+    if (n_parts < 1 || n_parts > 64)
+        return fail(MESH_ATTN_ERR_INVALID, "lse_merge: n_parts must be in 1..64");
+    if (rows < 0) return fail(MESH_ATTN_ERR_INVALID, "lse_merge: rows must be >= 0");
+    if (dtype != MESH_ATTN_BF16 && dtype != MESH_ATTN_F32)
+        return fail(MESH_ATTN_ERR_INVALID, "lse_merge: unknown dtype");
+    const int vec = dtype == MESH_ATTN_BF16 ? 8 : 4;
+    if (head_dim < 8 || head_dim > 512 || head_dim % vec != 0)
+        return fail(MESH_ATTN_ERR_INVALID, "lse_merge: head_dim must be a multiple of 8 (bf16) "
+                                           "or 4 (f32) in 8..512");
+    if (o_parts == nullptr || lse_parts == nullptr || o_out == nullptr)
+        return fail(MESH_ATTN_ERR_INVALID, "lse_merge: NULL tensor pointer");
+    if (!aligned16(o_parts) || !aligned16(o_out) ||
+        (reinterpret_cast<uintptr_t>(lse_parts) & 3u) != 0 ||
+        (lse_out != nullptr && (reinterpret_cast<uintptr_t>(lse_out) & 3u) != 0))
+        return fail(MESH_ATTN_ERR_INVALID, "lse_merge: misaligned pointer");
+    if (rows > (INT64_MAX / 64) / head_dim)
+        return fail(MESH_ATTN_ERR_INVALID, "lse_merge: rows too large");
+    if (rows == 0) {
+        clear_error();
+        return MESH_ATTN_OK;
+    }
+    const hipError_t e = launch_lse_merge(n_parts, rows, head_dim, dtype, o_parts, lse_parts,
+                                          o_out, lse_out, static_cast<hipStream_t>(hip_stream));
+    return hip_status(e, "lse_merge: kernel launch failed");
+}
+
+extern "C" const char* mesh_attn_status_string(int status) {
+    switch (status) {
+        case MESH_ATTN_OK: return "ok";
+        case MESH_ATTN_ERR_INVALID: return "invalid argument";
+        case MESH_ATTN_ERR_CAPACITY: return "output capacity too small";
+        case MESH_ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+        case MESH_ATTN_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+extern "C" const char* mesh_attn_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" int32_t mesh_attn_version(void) { return 100; }

@@ -1,0 +1,63 @@
+// Internal interface between the C-ABI layer (api.cpp) and the HIP kernels.
+// Not installed; the public interface is include/mesh_attn.h.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace mesh_attn {
+
+constexpr int kMaxQSlots = 64;
+constexpr int kMaxKvSlots = 64;
+constexpr int kMaxBlocks = 1024;
+
+// Block classes as stored in the packed schedule (same values as the ABI).
+constexpr int kFull = 0;
+constexpr int kDiag = 1;
+constexpr int kSkip = 2;
+
+// Which KV slots each Q slot attends to, packed into the kernel arguments.
+// For Q slot s the entries blk[blk_off[s] .. blk_off[s+1]) are
+// (kv_slot << 2) | kind, non-SKIP blocks only, in KV-slot (rotation) order.
+// q_order lists Q slots heaviest first (FULL = 1, DIAG = 1/2) so that the
+// longest work items are dispatched first.
+struct TileSchedule {
+    uint8_t q_order[kMaxQSlots];
+    uint16_t blk_off[kMaxQSlots + 1];
+    uint8_t blk[kMaxBlocks];
+};
+
+// Arguments of one tile-forward launch.  The grid is a flat list of work
+// items (Q slot rank, token block, KV head, query-head group); KV head varies
+// fastest so that work items sharing K/V land on the same XCD.
+struct TileParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int32_t part_len;      // L
+    int32_t heads_q;       // H_q
+    int32_t heads_kv;      // H_kv
+    int32_t group;         // G = H_q / H_kv
+    int32_t heads_per_wg;  // query heads of one KV group handled by a workgroup
+    int32_t tok_groups;    // 32-token row groups per workgroup (waves / heads_per_wg)
+    int32_t n_tok_blocks;  // ceil(L / (32 * tok_groups))
+    int32_t n_head_groups; // G / heads_per_wg
+    int32_t n_q_slots;
+    float scale_log2e;     // softmax_scale * log2(e)
+    TileSchedule sched;
+};
+
+// Number of waves per workgroup of the tile kernels.
+constexpr int kTileWaves = 4;
+
+hipError_t launch_tile_fwd_bf16(const TileParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_tile_fwd_f32(const TileParams& p, int head_dim, hipStream_t stream);
+
+hipError_t launch_lse_merge(int n_parts, int64_t rows, int head_dim, int dtype,
+                            const void* o_parts, const float* lse_parts, void* o_out,
+                            float* lse_out, hipStream_t stream);
+
+}  // namespace mesh_attn

@@ -1,0 +1,71 @@
+// Device helpers shared by the tile-forward kernels: work-item decoding, the
+// causal/ragged mask and the online-softmax state.
+//
+// Online softmax (ring-attention page, log-sum-exp section; FlashAttention is
+// cited on the mlsanity page): each query row keeps a running maximum m and a
+// running exponent sum l; when a new block of scores raises the maximum, the
+// accumulated output and l are rescaled by exp(m_old - m_new).  Scores are
+// kept in base 2: x2 = x * scale * log2(e), so exp(scale*x - m) becomes
+// exp2(x2 - m2) and one v_exp_f32 per score suffices.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace mesh_attn {
+namespace dev {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// Value of the same register in lane (l ^ 32), combined with op.
+__device__ __forceinline__ float max_with_partner(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float add_with_partner(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// One workgroup's share of a tile.
+struct WorkItem {
+    int q_slot;
+    int kv_head;
+    int head;      // query head of this wave
+    int wg_tok0;   // first token (partition offset) of the workgroup
+    int wave_tok0; // first token of this wave's 32 rows
+    int wg_tok_end;  // one past the workgroup's last valid token (<= L)
+};
+
+// blockIdx.x -> work item.  KV head varies fastest, then query-head group,
+// then token block (highest first: in a DIAG block later tokens see more
+// keys), then Q slot in heaviest-first order.
+__device__ __forceinline__ WorkItem decode_work(const TileParams& p, int wave) {
+    int lam = blockIdx.x;
+    WorkItem w;
+    w.kv_head = lam % p.heads_kv;
+    lam /= p.heads_kv;
+    const int hg = lam % p.n_head_groups;
+    lam /= p.n_head_groups;
+    const int tbi = lam % p.n_tok_blocks;
+    const int rank = lam / p.n_tok_blocks;
+    w.q_slot = p.sched.q_order[rank];
+    const int tb = p.n_tok_blocks - 1 - tbi;
+    const int h_in = wave % p.heads_per_wg;
+    const int tg = wave / p.heads_per_wg;
+    w.head = w.kv_head * p.group + hg * p.heads_per_wg + h_in;
+    w.wg_tok0 = tb * 32 * p.tok_groups;
+    w.wave_tok0 = w.wg_tok0 + 32 * tg;
+    w.wg_tok_end = min(p.part_len, w.wg_tok0 + 32 * p.tok_groups);
+    return w;
+}
+
+}  // namespace dev
+}  // namespace mesh_attn

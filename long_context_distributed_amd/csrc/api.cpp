@@ -164,9 +164,12 @@ extern "C" int mesh_attn_tile_fwd(const mesh_attn_tile_desc* desc, const void* q
     p.heads_q = d.heads_q;
     p.heads_kv = d.heads_kv;
     p.group = d.heads_q / d.heads_kv;
-    p.heads_per_wg = gcd(p.group, kTileWaves);
-    p.tok_groups = kTileWaves / p.heads_per_wg;
-    p.n_tok_blocks = (d.part_len + 32 * p.tok_groups - 1) / (32 * p.tok_groups);
+    const int waves = d.dtype == MESH_ATTN_BF16 ? kTileWavesBf16 : kTileWavesF32;
+    p.heads_per_wg = gcd(p.group, waves);
+    p.tok_groups = waves / p.heads_per_wg;
+    p.wave_rows = d.dtype == MESH_ATTN_BF16 ? kWaveRowsBf16 : kWaveRowsF32;
+    const int wg_rows = p.wave_rows * p.tok_groups;
+    p.n_tok_blocks = (d.part_len + wg_rows - 1) / wg_rows;
     p.n_head_groups = p.group / p.heads_per_wg;
     p.n_q_slots = d.n_q_slots;
     p.scale_log2e = d.softmax_scale * 1.4426950408889634f;

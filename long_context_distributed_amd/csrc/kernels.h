@@ -2,6 +2,7 @@
 // Not installed; the public interface is include/mesh_attn.h.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime_api.h>
@@ -23,10 +24,19 @@ constexpr int kSkip = 2;
 // q_order lists Q slots heaviest first (FULL = 1, DIAG = 1/2) so that the
 // longest work items are dispatched first.
 struct TileSchedule {
+    uint8_t blk[kMaxBlocks];  // first, so that it is 4-byte aligned (read as dwords)
     uint8_t q_order[kMaxQSlots];
-    uint16_t blk_off[kMaxQSlots + 1];
-    uint8_t blk[kMaxBlocks];
+    uint16_t blk_off[kMaxQSlots + 2];  // one spare entry keeps the size a multiple of 4
 };
+
+// Entry i of the packed schedule, read as a dword so that a wave-uniform
+// index becomes a scalar load (there are no scalar byte loads on gfx9).
+__device__ __forceinline__ int sched_entry(const TileSchedule& s, int i) {
+    const uint32_t word = reinterpret_cast<const uint32_t*>(s.blk)[i >> 2];
+    return (word >> (8 * (i & 3))) & 0xff;
+}
+
+static_assert(sizeof(TileSchedule) % 4 == 0, "schedule size");
 
 // Arguments of one tile-forward launch.  The grid is a flat list of work
 // items (Q slot rank, token block, KV head, query-head group); KV head varies
@@ -42,16 +52,22 @@ struct TileParams {
     int32_t heads_kv;      // H_kv
     int32_t group;         // G = H_q / H_kv
     int32_t heads_per_wg;  // query heads of one KV group handled by a workgroup
-    int32_t tok_groups;    // 32-token row groups per workgroup (waves / heads_per_wg)
-    int32_t n_tok_blocks;  // ceil(L / (32 * tok_groups))
+    int32_t tok_groups;    // token row groups per workgroup (waves / heads_per_wg)
+    int32_t wave_rows;     // query rows (tokens) per wave: 64 for bf16, 32 for f32
+    int32_t n_tok_blocks;  // ceil(L / (wave_rows * tok_groups))
     int32_t n_head_groups; // G / heads_per_wg
     int32_t n_q_slots;
     float scale_log2e;     // softmax_scale * log2(e)
     TileSchedule sched;
 };
 
-// Number of waves per workgroup of the tile kernels.
-constexpr int kTileWaves = 4;
+static_assert(offsetof(TileParams, sched) % 4 == 0, "schedule must be dword aligned");
+
+// Waves per workgroup and query rows per wave of the tile kernels.
+constexpr int kTileWavesBf16 = 8;
+constexpr int kTileWavesF32 = 4;
+constexpr int kWaveRowsBf16 = 32;
+constexpr int kWaveRowsF32 = 32;
 
 hipError_t launch_tile_fwd_bf16(const TileParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_tile_fwd_f32(const TileParams& p, int head_dim, hipStream_t stream);

@@ -40,7 +40,7 @@ struct WorkItem {
     int kv_head;
     int head;      // query head of this wave
     int wg_tok0;   // first token (partition offset) of the workgroup
-    int wave_tok0; // first token of this wave's 32 rows
+    int wave_tok0; // first token of this wave's rows
     int wg_tok_end;  // one past the workgroup's last valid token (<= L)
 };
 
@@ -61,9 +61,9 @@ __device__ __forceinline__ WorkItem decode_work(const TileParams& p, int wave) {
     const int h_in = wave % p.heads_per_wg;
     const int tg = wave / p.heads_per_wg;
     w.head = w.kv_head * p.group + hg * p.heads_per_wg + h_in;
-    w.wg_tok0 = tb * 32 * p.tok_groups;
-    w.wave_tok0 = w.wg_tok0 + 32 * tg;
-    w.wg_tok_end = min(p.part_len, w.wg_tok0 + 32 * p.tok_groups);
+    w.wg_tok0 = tb * p.wave_rows * p.tok_groups;
+    w.wave_tok0 = w.wg_tok0 + p.wave_rows * tg;
+    w.wg_tok_end = min(p.part_len, w.wg_tok0 + p.wave_rows * p.tok_groups);
     return w;
 }
 

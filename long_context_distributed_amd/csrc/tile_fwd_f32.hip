@@ -27,7 +27,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BN = 32;  // keys per LDS tile
-constexpr int NW = kTileWaves;
+constexpr int NW = kTileWavesF32;
 constexpr int NT = NW * 64;
 
 template <int D>
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(NT, 2) void tile_fwd_f32_kernel(const TileParams p)
 
     const int b_end = p.sched.blk_off[w.q_slot + 1];
     for (int bi = p.sched.blk_off[w.q_slot]; bi < b_end; ++bi) {
-        const int ent = p.sched.blk[bi];
+        const int ent = sched_entry(p.sched, bi);
         const int kv_slot = ent >> 2;
         const bool diag = (ent & 3) == kDiag;
         const int n_end = diag ? w.wg_tok_end : L;

@@ -4,10 +4,19 @@ A step is one pass of the whole hot path over one synthetic tile: the host
 block list (tile geometry, KV-rotation order, causal classes), the tile
 forward (QK^T, mask, online softmax, PV, epilogue) and the LSE merge of the
 partial results of the query rows.  Inputs are resident in HBM before the
-timed region; the partial results that the mesh-row peers would return are
-produced once, untimed, by the same kernel on the sibling tiles.
+timed region.  The merge combines this GPU's fresh partial with the partials
+its mesh-row peers would return; those are synthetic (random outputs, finite
+log-sum-exp, and -inf exactly where the peer's tile has no visible key for the
+row), since the merge's cost depends only on their sizes and on which rows
+are dead.  Their correctness against real sibling tiles is what the parity
+tests check.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
+                    [--no-cpu-baseline] [--copy-calibration MIB]
+
+--copy-calibration runs one plain device copy of MIB MiB after the steps, so
+that a hardware-counter run can scale FETCH_SIZE / WRITE_SIZE by what they
+read for a copy of known size.
 
 Prints one JSON line on stdout (everything else goes to stderr).
 """
@@ -94,6 +103,7 @@ def main():
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's tile only: the hot path is one GPU's share of the "
@@ -124,27 +134,25 @@ def main():
     rows = n_tok * w.heads_q
     elt = 2 if w.dtype == "bf16" else 4
 
-    # Partial results the peers would return, produced once by the same kernel.
+    # Partials the peers would return: same shapes, -inf where the peer's
+    # tile holds no KV partition at or before the row's partition.
     if w.merge == "per_kv_part":
         n_parts, own = R, None
+        peer_kv = [[kp] for kp in kv_parts]
     else:
         n_parts, own = C, c
-    o_parts = torch.empty((n_parts, rows, d), dtype=q.dtype, device=dev)
-    l_parts = torch.empty((n_parts, rows), dtype=torch.float32, device=dev)
-    for i in range(n_parts):
-        if w.merge == "per_kv_part":
-            sub = [b for b in blocks if b[1] == i]
-            mat.tile_fwd(q, k, v, sub, w.part_len, scale, out=o_parts[i].view_as(q),
-                         lse=l_parts[i].view(n_tok, w.heads_q))
-        elif i != own:
+        peer_kv = []
+        for i in range(C):
             sb = mat.block_list(R, C, r, i, w.causal, w.kv_rotate)
-            skv = [b[3] for b in sb if b[0] == 0]
-            ks = workloads.gather(w, "k", skv, dev)
-            vs = workloads.gather(w, "v", skv, dev)
-            mat.tile_fwd(q, ks, vs, sb, w.part_len, scale, out=o_parts[i].view_as(q),
-                         lse=l_parts[i].view(n_tok, w.heads_q))
-            del ks, vs
-    torch.cuda.synchronize()
+            peer_kv.append([b[3] for b in sb if b[0] == 0])
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    o_parts = (0.05 * torch.randn((n_parts, rows, d), generator=gen, device=dev)).to(q.dtype)
+    l_parts = 10.0 + torch.randn((n_parts, rows), generator=gen, device=dev)
+    for i, kvp in enumerate(peer_kv):
+        for s_, qp in enumerate(q_parts):
+            if w.causal and not any(kp <= qp for kp in kvp):
+                l_parts[i].view(n_tok, w.heads_q)[s_ * w.part_len:(s_ + 1) * w.part_len] = -math.inf
     if own is not None:
         o_own, l_own = o_parts[own].view_as(q), l_parts[own].view(n_tok, w.heads_q)
     else:
@@ -152,9 +160,13 @@ def main():
         l_own = torch.empty((n_tok, w.heads_q), dtype=torch.float32, device=dev)
     o_m = torch.empty((rows, d), dtype=q.dtype, device=dev)
     l_m = torch.empty((rows,), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
 
     flops = tile_flops(blocks, w.part_len, w.heads_q, d)
     mbytes = merge_bytes(n_parts, rows, d, elt)
+    # Bytes when dead partial rows (lse = -inf) are not read, as the kernel does.
+    live = int(torch.isfinite(l_parts).sum().item())
+    mbytes_live = n_parts * rows * 4 + live * d * elt + rows * (d * elt + 4)
 
     ev = []
 
@@ -212,11 +224,18 @@ def main():
         "tile_fwd": {"ms": t_tile, "tflops": tile_tflops, "frac_peak": tile_tflops / peak,
                      "flops": flops},
         "lse_merge": {"ms": t_merge, "gbs": merge_gbs, "frac_hbm": merge_gbs / PEAK_HBM_GBS,
-                      "bytes": mbytes},
+                      "bytes": mbytes, "bytes_live_rows": mbytes_live,
+                      "gbs_live_rows": mbytes_live / (t_merge * 1e-3) / 1e9},
         "roofline": {"bound": "mfma", "achieved": tile_tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": tile_tflops / peak, "traffic": None,
                      "kernel": "tile_fwd_bf16_d128" if w.dtype == "bf16" else "tile_fwd_f32"},
     }
+    if a.copy_calibration > 0:
+        src = torch.empty(a.copy_calibration << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {a.copy_calibration} MiB read + written by one copy kernel")
     if not a.no_cpu_baseline:
         log("[bench] timing the oracle on host cores")
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, q_parts, kv_parts, a.cpu_budget)

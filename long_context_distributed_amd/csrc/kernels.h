@@ -64,7 +64,7 @@ struct TileParams {
 static_assert(offsetof(TileParams, sched) % 4 == 0, "schedule must be dword aligned");
 
 // Waves per workgroup and query rows per wave of the tile kernels.
-constexpr int kTileWavesBf16 = 8;
+constexpr int kTileWavesBf16 = 12;
 constexpr int kTileWavesF32 = 4;
 constexpr int kWaveRowsBf16 = 32;
 constexpr int kWaveRowsF32 = 32;

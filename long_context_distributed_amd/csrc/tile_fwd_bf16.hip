@@ -6,14 +6,17 @@
 // not at all; the result is a partial output and log-sum-exp per query row.
 //
 // Work decomposition
-//   workgroup = NW waves sharing one KV head (two per SIMD); each wave owns 32
-//               query rows of one query head.  With GQA (G > 1) the waves of a
-//               workgroup are the query heads of one KV group, so one K/V
+//   workgroup = 12 waves (three per SIMD) sharing one KV head; each wave owns
+//               32 query rows of one query head.  With GQA (G > 1) the waves
+//               of a workgroup are query heads of one KV group, so one K/V
 //               stream from memory serves all of them.
 //   K/V are streamed through LDS in tiles of 64 keys by the DMA path of
-//   buffer loads (memory -> LDS without registers), into one of two buffers
-//   while the waves compute on the other: one barrier per tile.  Rows past
-//   the end of a partition read as zero through the buffer's range check.
+//   buffer loads (memory -> LDS without registers), three tiles in flight,
+//   one barrier per tile.  Rows past the end of a partition read as zero
+//   through the buffer's range check.
+//   Within a wave the work runs over 32-key halves with a software pipeline:
+//   the QK^T MFMAs of half j+1 are issued next to the exponentials of half j,
+//   and the PV MFMAs of half j next to the row maximum of half j+1.
 //
 // Matrix-core formulation (v_mfma_f32_32x32x16_bf16, 64-lane waves)
 //   S^T = K Q^T: A = K tile (32 keys x 16 dims), B = Q^T (16 dims x 32 rows).
@@ -40,11 +43,14 @@
 //   K: [64 keys][128 dims]; chunk c of key row n at chunk c ^ (n & 15).
 //   V: [64 keys][128 dims]; chunk c of key row n at chunk c ^ (4 * (n & 3)).
 #include <hip/hip_runtime.h>
-
-#include <type_traits>
+#include <stdint.h>
 
 #include "kernels.h"
 #include "tile_common.hpp"
+
+// The DMA loads set M0 in inline assembly (see dma_tile); nothing else in
+// this file uses M0.
+#pragma clang diagnostic ignored "-Winline-asm"
 
 namespace mesh_attn {
 namespace {
@@ -62,14 +68,16 @@ constexpr int D = 128;      // head dim
 constexpr int BN = 64;      // keys per LDS tile
 constexpr int NW = kTileWavesBf16;
 constexpr int NT = NW * 64;
+constexpr int kNBuf = 3;                    // LDS tiles in flight
 constexpr int kTileBytes = BN * D * 2;      // 16 KiB per K or V tile
 constexpr int kBufBytes = 2 * kTileBytes;   // K then V
 constexpr float kShiftSlack = 8.0f;         // base-2 headroom before the shift moves
 constexpr int kRsrcWord3 = 0x00020000;      // buffer resource flags for gfx9 (raw, 32-bit)
-constexpr int kDmaPerWave = 2 * kTileBytes / (NT * 16);  // 16-byte DMA loads per lane per tile
+constexpr int kDmaRegions = 2 * kTileBytes / 1024;       // 1 KiB DMA loads per tile
+constexpr int kDmaPerWave = (kDmaRegions + NW - 1) / NW;  // per wave (the last may idle)
 
 static_assert(kWaveRowsBf16 == 32, "one 32-row block per wave");
-static_assert(2 * kTileBytes % (NT * 16) == 0, "DMA split");
+
 
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 #define LDS_AS __attribute__((address_space(3)))
@@ -96,7 +104,7 @@ __device__ __forceinline__ void init_lanes(Lanes& ln, int tid, int wave, int row
     const int lane = tid & 63, g = lane >> 5, r32 = lane & 31;
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
-        const int reg = wave + NW * i;          // 0..31
+        const int reg = min(wave + NW * i, kDmaRegions - 1);  // 0..31
         const int row = 4 * (reg & 15) + (lane >> 4);
         const int phys = lane & 15;
         const int logical = reg < 16 ? (phys ^ (row & 15)) : (phys ^ (4 * (row & 3)));
@@ -109,107 +117,119 @@ __device__ __forceinline__ void init_lanes(Lanes& ln, int tid, int wave, int row
     for (int t = 0; t < 4; ++t) {
         const int row = 4 * g + (s16 >> 2);
         const int chunk = 4 * (t ^ (s16 >> 2)) + 2 * half + ((s16 & 3) >> 1);
-        ln.v_rofs[t] = row * (D * 2) + chunk * 16 + (s16 & 1) * 8;
+        ln.v_rofs[t] = kTileBytes + row * (D * 2) + chunk * 16 + (s16 & 1) * 8;
     }
 }
 
-// Issues the DMA loads of keys n0..n0+63 (rows past the range read as zero)
-// into LDS buffer `buf`.
-__device__ __forceinline__ void dma_tile(const Lanes& ln, Rsrc kr, Rsrc vr, LDS_AS unsigned char* buf,
-                                         int wave) {
+// Buffer descriptor words (base, range in bytes) for the DMA loads below.
+__device__ __forceinline__ u32x4 rows_desc(const void* base, int rows, int row_bytes) {
+    const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+    const int n = rows > 0 ? (rows - 1) * row_bytes + D * 2 : 0;
+    return u32x4{static_cast<unsigned>(a), static_cast<unsigned>(a >> 32) & 0xffffu,
+                 static_cast<unsigned>(n), static_cast<unsigned>(kRsrcWord3)};
+}
+
+// Issues the DMA loads of one K/V tile into LDS buffer `buf` (rows past the
+// range read as zero).  Written as assembly on purpose: the compiler then
+// does not model these LDS writes, so it does not make reads of the other
+// buffers wait for them; completion is awaited explicitly (vmcnt) before the
+// barrier that publishes the tile.  M0 holds the LDS destination.
+__device__ __forceinline__ void dma_tile(const Lanes& ln, u32x4 kr, u32x4 vr, unsigned buf, int wave) {
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
         const int reg = wave + NW * i;
-        const Rsrc r = reg < 16 ? kr : vr;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)(buf + reg * 1024), 16,
-                                                 ln.dma_gofs[i], 0, 0, 0);
+        if (reg >= kDmaRegions) break;
+        const unsigned dst = __builtin_amdgcn_readfirstlane(buf + reg * 1024);
+        if (reg < 16)
+            asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                         :: "s"(dst), "v"(ln.dma_gofs[i]), "s"(kr) : "memory", "m0");
+        else
+            asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                         :: "s"(dst), "v"(ln.dma_gofs[i]), "s"(vr) : "memory", "m0");
     }
 }
-
-struct State {
-    bf16x8 qf[8];      // Q^T fragments, d-chunk c
-    f32x16 o[4];       // O^T accumulators, dims 32t..32t+31
-    float m;           // shift in use (scaled base-2 scores)
-    float l;           // exponent sum over this lane's keys
-};
 
 __device__ __forceinline__ bf16x4 read_tr(const LDS_AS unsigned char* p) {
     const bf16x4_raw r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_raw*)p);
     return __builtin_bit_cast(bf16x4, r);
 }
 
-// Attention of the wave's 32 rows over the 64 keys n0.. held in LDS buffer `buf`.
-template <bool MASK>
-__device__ __forceinline__ void tile_math(State& st, const Lanes& ln, const LDS_AS unsigned char* buf,
-                                          int n0, int L, bool diag, int wave_tok0, float c2) {
-    const int lane = threadIdx.x & 63, g = lane >> 5, r32 = lane & 31;
-    const LDS_AS unsigned char* sv = buf + kTileBytes;
+// S^T = K Q^T for the 32 keys of half h of the tile in `buf`.
+__device__ __forceinline__ f32x16 qk_half(const Lanes& ln, const bf16x8 (&qf)[8],
+                                          const LDS_AS unsigned char* buf, int h) {
+    f32x16 s;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        // S^T = K Q^T for keys n0+32h .. +31.
-        f32x16 s;
+    for (int i = 0; i < 16; ++i) s[i] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = 0.0f;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const bf16x8 ka = *reinterpret_cast<const LDS_AS bf16x8*>(buf + ln.k_rofs[c] + 8192 * h);
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.qf[c], s, 0, 0, 0);
-        }
+    for (int c = 0; c < 8; ++c) {
+        const bf16x8 ka = *reinterpret_cast<const LDS_AS bf16x8*>(buf + ln.k_rofs[c] + 8192 * h);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[c], s, 0, 0, 0);
+    }
+    return s;
+}
 
-        if (MASK) {  // causal diagonal and ragged tail: hide keys after the query or past L
-            const int u = wave_tok0 + r32;
+// O^T += V^T P^T for the 32 keys of half h of the tile in `buf`.
+__device__ __forceinline__ void pv_half(const Lanes& ln, f32x16 (&o)[4], const bf16x8 (&pb)[2],
+                                        const LDS_AS unsigned char* buf, int h) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int kk = n0 + 32 * h + 8 * (i >> 2) + 4 * g + (i & 3);
-                if (kk >= L || (diag && kk > u)) s[i] = kNegInf;
-            }
-        }
-
-        // Row maximum; move the shift only where a score outgrew it.
-        float mx = kNegInf;
+    for (int kk = 0; kk < 2; ++kk) {
+        const int ks = 2 * h + kk;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
-        const float m_cand = dev::max_with_partner(mx) * c2;
-        const bool need = m_cand > st.m + kShiftSlack;
-        if (__builtin_amdgcn_ballot_w64(need) != 0) {
-            const float m_new = need ? m_cand : st.m;
-            const float alpha = need ? dev::fast_exp2(st.m - m_new) : 1.0f;
-            st.m = m_new;
-            st.l *= alpha;
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) st.o[t][i] *= alpha;
-        }
-
-        // P = exp2(S*c - m) in bf16, laid out as the B operand of the PV MFMAs.
-        bf16x8 pb[2];
-        const float shift = st.m == kNegInf ? 0.0f : st.m;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float pv = dev::fast_exp2(__builtin_fmaf(s[i], c2, -shift));
-            st.l += pv;
-            pb[i >> 3][i & 7] = static_cast<__bf16>(pv);
-        }
-
-        // O^T += V^T P^T, 16 keys per MFMA.
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int ks = 2 * h + kk;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const bf16x4 va = read_tr(sv + ln.v_rofs[t] + ks * 4096);
-                const bf16x4 vb = read_tr(sv + ln.v_rofs[t] + ks * 4096 + 2048);
-                const bf16x8 a8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-                st.o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, pb[kk], st.o[t], 0, 0, 0);
-            }
+        for (int t = 0; t < 4; ++t) {
+            const bf16x4 va = read_tr(buf + ln.v_rofs[t] + ks * 4096);
+            const bf16x4 vb = read_tr(buf + ln.v_rofs[t] + ks * 4096 + 2048);
+            const bf16x8 a8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+            o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, pb[kk], o[t], 0, 0, 0);
         }
     }
 }
 
+// Causal diagonal and ragged tail: hide keys after the query or past L.
+__device__ __forceinline__ void mask_half(f32x16& s, int key0, int L, bool diag, int u) {
+    const int g = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int kk = key0 + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (kk >= L || (diag && kk > u)) s[i] = kNegInf;
+    }
+}
+
+__device__ __forceinline__ float row_max(const f32x16& s) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    return dev::max_with_partner(mx);
+}
+
+// Moves the shift where a row's new maximum (scaled) outgrew it by the slack,
+// rescaling O and l.  Wave-uniform branch: rarely taken after the first half.
+__device__ __forceinline__ void update_shift(float m_cand, float& m, float& l, f32x16 (&o)[4]) {
+    const bool need = m_cand > m + kShiftSlack;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float m_new = need ? m_cand : m;
+        const float alpha = need ? dev::fast_exp2(m - m_new) : 1.0f;
+        m = m_new;
+        l *= alpha;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+    }
+}
+
+// P = exp2(S*c - m) in bf16, laid out as the B operand of the PV MFMAs; l += sum P.
+__device__ __forceinline__ void softmax_half(const f32x16& s, float c2, float m, float& l, bf16x8 (&pb)[2]) {
+    const float shift = m == kNegInf ? 0.0f : m;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float pv = dev::fast_exp2(__builtin_fmaf(s[i], c2, -shift));
+        l += pv;
+        pb[i >> 3][i & 7] = static_cast<__bf16>(pv);
+    }
+}
+
 __global__ __launch_bounds__(NT, 1) void tile_fwd_bf16_d128(const TileParams p) {
-    __shared__ __attribute__((aligned(1024))) unsigned char smem0[kBufBytes];
-    __shared__ __attribute__((aligned(1024))) unsigned char smem1[kBufBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kNBuf * kBufBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -222,86 +242,127 @@ __global__ __launch_bounds__(NT, 1) void tile_fwd_bf16_d128(const TileParams p) 
     const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (size_t)w.kv_head * D;
     const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (size_t)w.kv_head * D;
     const size_t slot_elems = (size_t)L * p.heads_kv * D;
+    const int u = w.wave_tok0 + r32;  // this lane's query offset in its partition
 
     Lanes ln;
     init_lanes(ln, tid, wave, row_bytes);
 
-    State st;
+    bf16x8 qf[8];  // Q^T fragments, d-chunk c: q[u][h][16c + 8g .. +7] (zero past L)
     {
-        // Q rows of this wave (rows at or past L read as zero).
         const int qrow_bytes = p.heads_q * D * 2;
         const __bf16* q0 = reinterpret_cast<const __bf16*>(p.q) +
                            ((size_t)(w.q_slot * L + w.wave_tok0) * p.heads_q + w.head) * D;
         const Rsrc qr = rows_rsrc(q0, L - w.wave_tok0, qrow_bytes);
 #pragma unroll
         for (int c = 0; c < 8; ++c)
-            st.qf[c] = __builtin_bit_cast(
+            qf[c] = __builtin_bit_cast(
                 bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, r32 * qrow_bytes + (16 * c + 8 * g) * 2,
                                                               0, 0));
     }
+    f32x16 o[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) st.o[t][i] = 0.0f;
-    st.m = kNegInf;
-    st.l = 0.0f;
-    const int wave_last_tok = min(L, w.wave_tok0 + 32) - 1;
+        for (int i = 0; i < 16; ++i) o[t][i] = 0.0f;
+    float m = kNegInf;  // shift in use (scaled base-2 scores)
+    float l = 0.0f;     // exponent sum over this lane's keys
 
     const int b_beg = p.sched.blk_off[w.q_slot];
     const int b_end = p.sched.blk_off[w.q_slot + 1];
 
-    // The tiles of this Q slot form one sequence over (block, key tile); the
-    // next tile streams into the other LDS buffer while this one is computed.
-    int bi = b_beg, n0 = 0;
-    auto issue = [&](int bi_, int n0_, LDS_AS unsigned char* buf) {
-        const size_t off = (size_t)(sched_entry(p.sched, bi_) >> 2) * slot_elems + (size_t)n0_ * p.heads_kv * D;
-        dma_tile(ln, rows_rsrc(kbase + off, L - n0_, row_bytes),
-                 rows_rsrc(vbase + off, L - n0_, row_bytes), buf, wave);
+    // The tiles of this Q slot form one sequence over (block, key tile); tile
+    // t lives in LDS buffer t % 3.  The work runs over 32-key halves j with a
+    // software pipeline: the QK^T MFMAs of half j+1 are issued together with
+    // the exponentials of half j, and the PV MFMAs of half j together with the
+    // row maximum of half j+1.  Stepping into tile t+1, the waves wait for its
+    // DMA and meet at a barrier; tile t's V is still read after it (the PV of
+    // its last half), so the DMA started there, for tile t+2, goes into tile
+    // t-1's buffer, which every wave finished before the barrier.
+    auto tile_end = [&](int bi_) {
+        return (sched_entry(p.sched, bi_) & 3) == kDiag ? w.wg_tok_end : L;
     };
     auto advance = [&](int& bi_, int& n0_) {
         n0_ += BN;
-        const int end = (sched_entry(p.sched, bi_) & 3) == kDiag ? w.wg_tok_end : L;
-        if (n0_ >= end) {
+        if (n0_ >= tile_end(bi_)) {
             ++bi_;
             n0_ = 0;
         }
     };
+    const unsigned lds0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>((LDS_AS unsigned char*)smem));
+    auto issue = [&](int bi_, int n0_, int buf_) {
+        const size_t off = (size_t)(sched_entry(p.sched, bi_) >> 2) * slot_elems + (size_t)n0_ * p.heads_kv * D;
+        dma_tile(ln, rows_desc(kbase + off, L - n0_, row_bytes), rows_desc(vbase + off, L - n0_, row_bytes),
+                 lds0 + buf_ * kBufBytes, wave);
+    };
+    auto masked_half = [&](f32x16& sc, int bi_, int key0) {
+        const bool diag = (sched_entry(p.sched, bi_) & 3) == kDiag;
+        if ((diag && key0 + 31 > w.wave_tok0) || key0 + 32 > L) mask_half(sc, key0, L, diag, u);
+    };
+    auto vmcnt0_barrier = [&]() {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
 
     if (b_beg < b_end) {
-        issue(bi, n0, (LDS_AS unsigned char*)smem0);
-        __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this thread's DMA has landed
-        __syncthreads();
-        // One step: start the next tile's DMA into the other buffer, compute
-        // on buffer BUF, wait for the DMA, barrier.  False after the last tile.
-        auto step = [&](auto buf_tag) -> bool {
-            constexpr int BUF = decltype(buf_tag)::value;
-            LDS_AS unsigned char* cur = (LDS_AS unsigned char*)(BUF == 0 ? smem0 : smem1);
-            LDS_AS unsigned char* nxt = (LDS_AS unsigned char*)(BUF == 0 ? smem1 : smem0);
-            int nbi = bi, nn0 = n0;
-            advance(nbi, nn0);
-            const bool has_next = nbi < b_end;
-            if (has_next) issue(nbi, nn0, nxt);
-            const bool diag = (sched_entry(p.sched, bi) & 3) == kDiag;
-            if (!(diag && n0 > wave_last_tok)) {
-                if ((diag && n0 + BN - 1 > w.wave_tok0) || n0 + BN > L)
-                    tile_math<true>(st, ln, cur, n0, L, diag, w.wave_tok0, c2);
-                else
-                    tile_math<false>(st, ln, cur, n0, L, diag, w.wave_tok0, c2);
+        const LDS_AS unsigned char* lds = (const LDS_AS unsigned char*)smem;
+        int bi = b_beg, n0 = 0;    // tile t
+        int bi1 = bi, n01 = n0;    // tile t+1
+        advance(bi1, n01);
+        issue(bi, n0, 0);
+        vmcnt0_barrier();
+        if (bi1 < b_end) issue(bi1, n01, 1);
+        int buf = 0, h = 0;
+
+        f32x16 s = qk_half(ln, qf, lds, 0);
+        masked_half(s, bi, n0);
+        update_shift(row_max(s) * c2, m, l, o);
+
+        for (;;) {
+            int nbuf = buf, nbi = bi, nn0 = n0, bi2 = bi1, n02 = n01;
+            if (h == 1) {
+                if (bi1 >= b_end) break;
+                vmcnt0_barrier();  // tile t+1 has landed in every wave's view
+                nbuf = buf == 2 ? 0 : buf + 1;
+                nbi = bi1;
+                nn0 = n01;
+                advance(bi2, n02);
+                if (bi2 < b_end) issue(bi2, n02, buf == 0 ? 2 : buf - 1);
             }
-            if (!has_next) return false;
-            __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
-            __syncthreads();
-            bi = nbi;
-            n0 = nn0;
-            return true;
-        };
-        while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
+            const int nh = h ^ 1;
+            // QK^T of half j+1 with the exponentials of half j: the 8 K
+            // fragment reads go first, then each MFMA is followed by a share
+            // of the softmax arithmetic (scheduling groups, in order).
+            f32x16 s_next = qk_half(ln, qf, lds + nbuf * kBufBytes, nh);
+            bf16x8 pb[2];
+            softmax_half(s, c2, m, l, pb);
+            // Keep the softmax in this region (not sunk past the mask branch
+            // to its use in the PV MFMAs).
+            asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(l));
+
+            masked_half(s_next, nbi, nn0 + 32 * nh);
+            // PV of half j with the maximum of half j+1.
+            const float m_cand = row_max(s_next) * c2;
+            pv_half(ln, o, pb, lds + buf * kBufBytes, h);
+
+            update_shift(m_cand, m, l, o);
+            s = s_next;
+            if (h == 1) {
+                buf = nbuf;
+                bi = nbi;
+                n0 = nn0;
+                bi1 = bi2;
+                n01 = n02;
+            }
+            h = nh;
         }
+        // Last half.
+        bf16x8 pb[2];
+        softmax_half(s, c2, m, l, pb);
+        pv_half(ln, o, pb, lds + buf * kBufBytes, h);
     }
 
     // Epilogue: O = O_acc / l, lse = ln(2) * (m + log2 l); empty rows -> (0, -inf).
-    const int u = w.wave_tok0 + r32;
-    const float l_tot = dev::add_with_partner(st.l);
+    const float l_tot = dev::add_with_partner(l);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     if (u < L) {
         const size_t q_row = (size_t)(w.q_slot * L + u) * p.heads_q + w.head;
@@ -312,10 +373,10 @@ __global__ __launch_bounds__(NT, 1) void tile_fwd_bf16_d128(const TileParams p) 
             for (int ib = 0; ib < 4; ++ib) {
                 bf16x4 ov;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) ov[j] = static_cast<__bf16>(st.o[t][4 * ib + j] * inv);
+                for (int j = 0; j < 4; ++j) ov[j] = static_cast<__bf16>(o[t][4 * ib + j] * inv);
                 *reinterpret_cast<bf16x4*>(op + 32 * t + 8 * ib + 4 * g) = ov;
             }
-        if (g == 0) p.lse[q_row] = l_tot > 0.0f ? (st.m + __log2f(l_tot)) * dev::kLn2 : kNegInf;
+        if (g == 0) p.lse[q_row] = l_tot > 0.0f ? (m + __log2f(l_tot)) * dev::kLn2 : kNegInf;
     }
 }
 

@@ -104,15 +104,18 @@ def test_deterministic_and_canaries():
     assert torch.all(big_l[:pad] == 3.5) and torch.all(big_l[-pad:] == 3.5), "lse canary hit"
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64), ("f32", 128)])
-def test_merge_matches_oracle(dtype, d):
+@pytest.mark.parametrize("dtype,d,n", [("bf16", 128, 5), ("f32", 64, 5), ("bf16", 64, 5),
+                                       ("f32", 128, 5), ("bf16", 128, 1), ("bf16", 128, 2),
+                                       ("bf16", 128, 16), ("bf16", 128, 20), ("f32", 64, 33),
+                                       ("bf16", 24, 3), ("f32", 12, 7)])
+def test_merge_matches_oracle(dtype, d, n):
     import torch
     import long_context_distributed_amd as mat
     r = np.random.default_rng(5)
-    n, rows = 5, 3001
+    rows = 3001
     o = r.standard_normal((n, rows, d))
     lse = 4.0 * r.standard_normal((n, rows))
-    lse[1, ::3] = -np.inf          # dead partial rows
+    lse[min(1, n - 1), ::3] = -np.inf  # dead partial rows
     lse[:, 7] = -np.inf            # an all-dead row
     lse[:, 9] = 80.0               # large equal values
     o[np.isneginf(lse)] = np.nan   # rows of dead partials must not be read

@@ -36,8 +36,44 @@ PEAK_F32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 
+# Kernel sources whose hash keys the counter-derived traffic in profiles/.
+KERNEL_SOURCES = {
+    "tile_fwd_bf16_d128": ["tile_fwd_bf16.hip", "tile_common.hpp", "kernels.h"],
+    "tile_fwd_f32": ["tile_fwd_f32.hip", "tile_common.hpp", "kernels.h"],
+    "lse_merge_kernel": ["lse_merge.hip", "kernels.h"],
+}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha256(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "long_context_distributed_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the rocprofv3 counter
+    summaries in profiles/ (FETCH_SIZE and WRITE_SIZE scaled by a copy of
+    known size), or None when no summary matches the current kernel source."""
+    import glob
+    want = source_sha256(kernel)
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        fields = {}
+        with open(path) as f:
+            for line in f:
+                if ":" in line and line.startswith("- "):
+                    key, val = line[2:].split(":", 1)
+                    fields[key.strip()] = val.strip().strip("`")
+        if (fields.get("kernel") == kernel and fields.get("workload") == str(workload)
+                and fields.get("source_sha256") == want and "hbm_bytes_per_launch" in fields):
+            return float(fields["hbm_bytes_per_launch"])
+    return None
 
 
 def tile_flops(blocks, part_len, heads_q, head_dim):
@@ -199,6 +235,7 @@ def main():
     tile_tflops = flops / (t_tile * 1e-3) / 1e12
     merge_gbs = mbytes / (t_merge * 1e-3) / 1e9
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    tile_kernel = "tile_fwd_bf16_d128" if w.dtype == "bf16" else "tile_fwd_f32"
     log(f"[bench] tile {t_tile:.3f} ms = {tile_tflops:.1f} TFLOP/s ({100 * tile_tflops / peak:.1f}% "
         f"of {peak}); merge {t_merge:.3f} ms = {merge_gbs:.0f} GB/s "
         f"({100 * merge_gbs / PEAK_HBM_GBS:.1f}% of HBM); step {ms_step:.3f} ms")
@@ -225,10 +262,12 @@ def main():
                      "flops": flops},
         "lse_merge": {"ms": t_merge, "gbs": merge_gbs, "frac_hbm": merge_gbs / PEAK_HBM_GBS,
                       "bytes": mbytes, "bytes_live_rows": mbytes_live,
-                      "gbs_live_rows": mbytes_live / (t_merge * 1e-3) / 1e9},
+                      "gbs_live_rows": mbytes_live / (t_merge * 1e-3) / 1e9,
+                      "traffic": measured_traffic("lse_merge_kernel", a.workload)},
         "roofline": {"bound": "mfma", "achieved": tile_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": tile_tflops / peak, "traffic": None,
-                     "kernel": "tile_fwd_bf16_d128" if w.dtype == "bf16" else "tile_fwd_f32"},
+                     "frac": tile_tflops / peak, "traffic": measured_traffic(tile_kernel, a.workload),
+                     "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE)",
+                     "kernel": tile_kernel},
     }
     if a.copy_calibration > 0:
         src = torch.empty(a.copy_calibration << 20, dtype=torch.uint8, device=dev)

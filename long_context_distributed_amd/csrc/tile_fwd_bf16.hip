@@ -45,6 +45,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 #include "tile_common.hpp"
 
@@ -68,7 +70,7 @@ constexpr int D = 128;      // head dim
 constexpr int BN = 64;      // keys per LDS tile
 constexpr int NW = kTileWavesBf16;
 constexpr int NT = NW * 64;
-constexpr int kNBuf = 3;                    // LDS tiles in flight
+constexpr int kNBuf = 5;                    // LDS tiles in flight (5 x 32 KiB = all of LDS)
 constexpr int kTileBytes = BN * D * 2;      // 16 KiB per K or V tile
 constexpr int kBufBytes = 2 * kTileBytes;   // K then V
 constexpr float kShiftSlack = 8.0f;         // base-2 headroom before the shift moves
@@ -294,10 +296,6 @@ __global__ __launch_bounds__(NT, 1) void tile_fwd_bf16_d128(const TileParams p) 
         dma_tile(ln, rows_desc(kbase + off, L - n0_, row_bytes), rows_desc(vbase + off, L - n0_, row_bytes),
                  lds0 + buf_ * kBufBytes, wave);
     };
-    auto masked_half = [&](f32x16& sc, int bi_, int key0) {
-        const bool diag = (sched_entry(p.sched, bi_) & 3) == kDiag;
-        if ((diag && key0 + 31 > w.wave_tok0) || key0 + 32 > L) mask_half(sc, key0, L, diag, u);
-    };
     auto vmcnt0_barrier = [&]() {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -305,60 +303,83 @@ __global__ __launch_bounds__(NT, 1) void tile_fwd_bf16_d128(const TileParams p) 
 
     if (b_beg < b_end) {
         const LDS_AS unsigned char* lds = (const LDS_AS unsigned char*)smem;
+        auto is_diag = [&](int bi_) { return (sched_entry(p.sched, bi_) & 3) == kDiag; };
+        auto needs_mask = [&](bool diag_, int key0) {
+            return (diag_ && key0 + 31 > w.wave_tok0) || key0 + 32 > L;
+        };
+        auto next_buf = [](int b) { return b == kNBuf - 1 ? 0 : b + 1; };
+        // DMA cursor: the next tile to load and its buffer.
+        int dbi = b_beg, dn0 = 0, dbuf = 0;
+        auto issue_next = [&]() {
+            if (dbi < b_end) {
+                issue(dbi, dn0, dbuf);
+                advance(dbi, dn0);
+                dbuf = next_buf(dbuf);
+            }
+        };
         int bi = b_beg, n0 = 0;    // tile t
+        bool dg = is_diag(bi);
         int bi1 = bi, n01 = n0;    // tile t+1
         advance(bi1, n01);
-        issue(bi, n0, 0);
+        int t = 0, buf = 0;
+        issue_next();  // tiles 0 and 1
+        issue_next();
         vmcnt0_barrier();
-        if (bi1 < b_end) issue(bi1, n01, 1);
-        int buf = 0, h = 0;
+        issue_next();  // tiles 2 and 3
+        issue_next();
 
         f32x16 s = qk_half(ln, qf, lds, 0);
-        masked_half(s, bi, n0);
+        if (needs_mask(dg, n0)) mask_half(s, n0, L, dg, u);
         update_shift(row_max(s) * c2, m, l, o);
 
-        for (;;) {
-            int nbuf = buf, nbi = bi, nn0 = n0, bi2 = bi1, n02 = n01;
-            if (h == 1) {
-                if (bi1 >= b_end) break;
-                vmcnt0_barrier();  // tile t+1 has landed in every wave's view
-                nbuf = buf == 2 ? 0 : buf + 1;
-                nbi = bi1;
-                nn0 = n01;
-                advance(bi2, n02);
-                if (bi2 < b_end) issue(bi2, n02, buf == 0 ? 2 : buf - 1);
-            }
-            const int nh = h ^ 1;
-            // QK^T of half j+1 with the exponentials of half j: the 8 K
-            // fragment reads go first, then each MFMA is followed by a share
-            // of the softmax arithmetic (scheduling groups, in order).
-            f32x16 s_next = qk_half(ln, qf, lds + nbuf * kBufBytes, nh);
+        // One pipeline step from half H of the tile in `cur` to the next half
+        // (half 1 of the same tile, or half 0 of the next tile in `nxt`).
+        auto step = [&](auto h_tag, const LDS_AS unsigned char* cur, const LDS_AS unsigned char* nxt,
+                        bool mask_next, bool diag_next, int key0_next) {
+            constexpr int H = decltype(h_tag)::value;
+            // QK^T of the next half with the exponentials of this half.
+            f32x16 s_next = qk_half(ln, qf, nxt, H ^ 1);
             bf16x8 pb[2];
             softmax_half(s, c2, m, l, pb);
-            // Keep the softmax in this region (not sunk past the mask branch
-            // to its use in the PV MFMAs).
+            // Keep the softmax here (not sunk past the mask branch to the PV).
             asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(l));
-
-            masked_half(s_next, nbi, nn0 + 32 * nh);
-            // PV of half j with the maximum of half j+1.
+            if (mask_next) mask_half(s_next, key0_next, L, diag_next, u);
+            // PV of this half with the maximum of the next half.
             const float m_cand = row_max(s_next) * c2;
-            pv_half(ln, o, pb, lds + buf * kBufBytes, h);
-
+            pv_half(ln, o, pb, cur, H);
             update_shift(m_cand, m, l, o);
             s = s_next;
-            if (h == 1) {
-                buf = nbuf;
-                bi = nbi;
-                n0 = nn0;
-                bi1 = bi2;
-                n01 = n02;
+        };
+
+        for (;;) {
+            const LDS_AS unsigned char* cur = lds + buf * kBufBytes;
+            // Half 0 -> half 1 of tile t.
+            step(std::integral_constant<int, 0>{}, cur, cur, needs_mask(dg, n0 + 32), dg, n0 + 32);
+            if (bi1 >= b_end) break;
+            // Into tile t+1.  Every second tile the waves wait for their DMA
+            // (tiles t+1 and t+2 were loaded together) and meet at a barrier;
+            // every wave has then finished tile t-1, so the buffers of tiles
+            // t-2 and t-1 take tiles t+3 and t+4.
+            if ((t & 1) == 1) {
+                vmcnt0_barrier();
+                issue_next();
+                issue_next();
             }
-            h = nh;
+            const int nbuf = next_buf(buf);
+            const bool dg1 = is_diag(bi1);
+            step(std::integral_constant<int, 1>{}, cur, lds + nbuf * kBufBytes, needs_mask(dg1, n01), dg1,
+                 n01);
+            buf = nbuf;
+            ++t;
+            bi = bi1;
+            n0 = n01;
+            dg = dg1;
+            advance(bi1, n01);
         }
-        // Last half.
+        // Second half of the last tile.
         bf16x8 pb[2];
         softmax_half(s, c2, m, l, pb);
-        pv_half(ln, o, pb, lds + buf * kBufBytes, h);
+        pv_half(ln, o, pb, lds + buf * kBufBytes, 1);
     }
 
     // Epilogue: O = O_acc / l, lse = ln(2) * (m + log2 l); empty rows -> (0, -inf).

@@ -1,0 +1,111 @@
+"""The host C++ of the library (block list, argument validation, schedule
+packing) built a second time with AddressSanitizer and UBSan by g++, and
+driven through the same C ABI in a subprocess (CPU only).
+
+The device kernels are replaced by stubs that return an error, so even
+fully valid descriptors (with fake device addresses, never dereferenced)
+exercise the whole host path, including schedule packing, under the
+sanitizers.
+"""
+import os
+import shutil
+import subprocess
+import sys
+import textwrap
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "long_context_distributed_amd", "csrc")
+
+STUB = """
+#include "kernels.h"
+namespace mesh_attn {
+hipError_t launch_tile_fwd_bf16(const TileParams&, int, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_tile_fwd_f32(const TileParams&, int, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_lse_merge(int, int64_t, int, int, const void*, const float*, void*, float*,
+                            hipStream_t) { return hipErrorNoDevice; }
+}
+"""
+
+DRIVER = textwrap.dedent("""
+    import ctypes, itertools, sys
+    sys.path.insert(0, {root!r})
+    import oracle
+    from long_context_distributed_amd import _lib
+    _lib.LIB_PATH = {lib!r}
+    lib = _lib.load()
+    n = ctypes.c_int32(0)
+    for R, C in itertools.product(range(1, 7), repeat=2):
+        arr = (_lib.Block * (R * C))()
+        for r, c in itertools.product(range(R), range(C)):
+            for causal, rot in itertools.product((0, 1), repeat=2):
+                assert lib.mesh_attn_block_list(R, C, r, c, causal, rot, arr, R * C, ctypes.byref(n)) == 0
+                got = [(b.q_slot, b.kv_slot, b.q_part, b.kv_part, b.kind) for b in arr]
+                assert got == oracle.block_list_ref(R, C, r, c, causal, rot)
+    FAKE = 0x100000
+    def desc(blocks, dtype=0, L=64, nq=2, nkv=2, hq=4, hkv=2, d=128, scale=0.1):
+        arr = (_lib.Block * max(1, len(blocks)))(*[_lib.Block(*b) for b in blocks])
+        dd = _lib.TileDesc(dtype, L, nq, nkv, hq, hkv, d, scale, arr, len(blocks))
+        dd._keep = arr
+        return dd
+    # valid descriptors reach the (stub) launch: full schedule packing under the sanitizers
+    for (R, C, r, c) in [(2, 2, 0, 0), (4, 4, 2, 2), (8, 8, 4, 4), (16, 4, 8, 2), (8, 8, 0, 7)]:
+        bl = oracle.block_list_ref(R, C, r, c, True, True)
+        for dtype, d in ((0, 128), (1, 64), (1, 128)):
+            st = lib.mesh_attn_tile_fwd(ctypes.byref(desc(bl, dtype=dtype, nq=C, nkv=R, d=d)),
+                                        FAKE, FAKE, FAKE, FAKE, FAKE, None)
+            assert st == _lib.ERR_HIP, st
+    # every invalid descriptor is rejected
+    bl = oracle.block_list_ref(2, 2, 0, 0, True, True)
+    for kw in (dict(dtype=7), dict(L=0), dict(nq=0), dict(nq=65), dict(hq=3), dict(scale=0.0),
+               dict(d=96)):
+        assert lib.mesh_attn_tile_fwd(ctypes.byref(desc(bl, **kw)), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      None) < 0
+    assert lib.mesh_attn_tile_fwd(ctypes.byref(desc(bl + [bl[0]])), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  None) == _lib.ERR_INVALID
+    big = [(s, j, s, 64 + j, 0) for s in range(32) for j in range(32)]   # 1024 blocks
+    assert lib.mesh_attn_tile_fwd(ctypes.byref(desc(big, nq=32, nkv=32)), FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, None) == _lib.ERR_HIP
+    assert lib.mesh_attn_lse_merge(8, 1 << 20, 128, 0, FAKE, FAKE, FAKE, FAKE, None) == _lib.ERR_HIP
+    assert lib.mesh_attn_lse_merge(0, 16, 128, 0, FAKE, FAKE, FAKE, FAKE, None) == _lib.ERR_INVALID
+    print("sanitized host path ok")
+""")
+
+
+def _runtime(name):
+    out = subprocess.run(["g++", f"-print-file-name={name}"], capture_output=True, text=True)
+    path = out.stdout.strip()
+    return path if os.path.isabs(path) and os.path.exists(path) else None
+
+
+@pytest.mark.skipif(shutil.which("g++") is None or not os.path.exists("/opt/rocm/include/hip"),
+                    reason="needs g++ and the HIP headers")
+def test_host_code_under_asan_and_ubsan(tmp_path):
+    asan, ubsan = _runtime("libasan.so"), _runtime("libubsan.so")
+    if not asan or not ubsan:
+        pytest.skip("sanitizer runtimes not installed")
+    stub = tmp_path / "stub.cpp"
+    stub.write_text(STUB)
+    lib = tmp_path / "libmeshattn_sanitized.so"
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fsanitize=address,undefined",
+           "-fno-omit-frame-pointer", "-fno-sanitize-recover=undefined", "-D__HIP_PLATFORM_AMD__",
+           "-I/opt/rocm/include", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "block_list.cpp"), str(stub),
+           "-o", str(lib), "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    env = dict(os.environ, LD_PRELOAD=f"{asan} {ubsan}", ASAN_OPTIONS="detect_leaks=0",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    res = subprocess.run([sys.executable, "-c", DRIVER.format(root=ROOT, lib=str(lib))],
+                         capture_output=True, text=True, env=env, timeout=300)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "sanitized host path ok" in res.stdout
+    assert "runtime error" not in res.stderr and "AddressSanitizer" not in res.stderr
+
+
+def test_bench_refuses_more_than_one_gpu():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr and res.stdout == ""

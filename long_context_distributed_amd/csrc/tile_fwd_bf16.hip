@@ -11,8 +11,9 @@
 //               of a workgroup are query heads of one KV group, so one K/V
 //               stream from memory serves all of them.
 //   K/V are streamed through LDS in tiles of 64 keys by the DMA path of
-//   buffer loads (memory -> LDS without registers), three tiles in flight,
-//   one barrier per tile.  Rows past the end of a partition read as zero
+//   buffer loads (memory -> LDS without registers) into five buffers (all of
+//   LDS); the waves meet at a barrier every second tile, where the DMA of the
+//   next two tiles starts.  Rows past the end of a partition read as zero
 //   through the buffer's range check.
 //   Within a wave the work runs over 32-key halves with a software pipeline:
 //   the QK^T MFMAs of half j+1 are issued next to the exponentials of half j,
@@ -79,7 +80,6 @@ constexpr int kDmaRegions = 2 * kTileBytes / 1024;       // 1 KiB DMA loads per 
 constexpr int kDmaPerWave = (kDmaRegions + NW - 1) / NW;  // per wave (the last may idle)
 
 static_assert(kWaveRowsBf16 == 32, "one 32-row block per wave");
-
 
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 #define LDS_AS __attribute__((address_space(3)))

@@ -15,6 +15,9 @@ with no blocking, no online softmax and no fusion:
   natural-log log-sum-exp of the scaled scores.
 * ``lse_merge_ref``  - the log-sum-exp weighted combination of partial
   (output, lse) pairs.
+* ``attention_bwd_ref`` / ``tile_bwd_ref`` / ``bwd_delta_ref`` - the gradients
+  of attention (dQ, dK, dV) split into the share of one tile's visible pairs,
+  given the rows' final lse and D = rowsum(dO * O).
 
 Every function here is pinned by CPU tests to something other than itself
 (library routines, closed forms, invariants, brute force); see the test files
@@ -24,10 +27,12 @@ named ``test_oracle_*.py``.
 from .block_list import FULL, DIAG, SKIP, block_list_ref, mesh_tile_sets_ref
 from .attention import attention_ref, tile_rows_ref, tile_positions_ref
 from .merge import lse_merge_ref
+from .backward import attention_bwd_ref, bwd_delta_ref, full_grads_ref, tile_bwd_ref
 
 __all__ = [
     "FULL", "DIAG", "SKIP",
     "block_list_ref", "mesh_tile_sets_ref",
     "attention_ref", "tile_rows_ref", "tile_positions_ref",
     "lse_merge_ref",
+    "attention_bwd_ref", "bwd_delta_ref", "full_grads_ref", "tile_bwd_ref",
 ]

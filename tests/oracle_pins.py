@@ -341,3 +341,139 @@ def check_block_list_kinds(block_list, R, C):
         _, qset, kvset = _tile_sets(block_list, R, C, r, c, False, False)
         assert qset == [r * C + t for t in range(C)], "contiguous Q set"
         assert kvset == [c * R + k for k in range(R)], "contiguous KV set"
+
+
+# --------------------------------------------------------------------------- backward
+
+def _torch_full_grads(q, k, v, do, q_pos, k_pos, causal, scale):
+    """Gradients of sum(O * dO) by torch autograd (float64, CPU), with lse
+    from torch.logsumexp and D from the autograd forward's output."""
+    import torch
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    tv = torch.tensor(v, requires_grad=True)
+    g = q.shape[1] // k.shape[1]
+    kk = tk.repeat_interleave(g, dim=1)              # [Nk, Hq, d]
+    vv = tv.repeat_interleave(g, dim=1)
+    s = scale * torch.einsum("ihd,jhd->hij", tq, kk)
+    if causal:
+        mask = torch.tensor(k_pos[None, :] <= q_pos[:, None])
+        s = s.masked_fill(~mask[None], float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    o = torch.einsum("hij,jhd->ihd", p, vv)
+    (o * torch.tensor(do)).sum().backward()
+    lse = torch.logsumexp(s, dim=-1).T.detach().numpy()
+    delta = (o.detach() * torch.tensor(do)).sum(-1).numpy()
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy(), lse, delta
+
+
+def check_bwd_autograd(bwd, causal, hq=4, hkv=2, nq=11, nk=11, d=16, seed=20):
+    """Whole contiguous matrix: the oracle's gradients equal torch autograd's."""
+    r = _rng(seed)
+    q, k, v = (r.standard_normal(s) for s in ((nq, hq, d), (nk, hkv, d), (nk, hkv, d)))
+    do = r.standard_normal((nq, hq, d))
+    qp, kp = np.arange(nq), np.arange(nk)
+    scale = 1.0 / math.sqrt(d)
+    rdq, rdk, rdv, lse, delta = _torch_full_grads(q, k, v, do, qp, kp, causal, scale)
+    dq, dk, dv = bwd(q, k, v, do, lse, delta, qp, kp, causal, scale)
+    for name, a, b in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        assert np.allclose(a, b, rtol=1e-10, atol=1e-11), f"{name} differs from torch autograd"
+
+
+def check_bwd_finite_differences(bwd, seed=21):
+    """Tiny case, positions not contiguous, causal: central differences of the
+    loss sum(O * dO), with O computed by brute force in pure Python (math.exp,
+    no max shift), match the oracle's gradients."""
+    r = _rng(seed)
+    nq, nk, hq, hkv, d = 3, 5, 2, 1, 3
+    q, k, v = (r.standard_normal(s) for s in ((nq, hq, d), (nk, hkv, d), (nk, hkv, d)))
+    do = r.standard_normal((nq, hq, d))
+    qp, kp = np.array([4, 7, 9]), np.array([0, 5, 6, 7, 9])
+    scale = 0.7
+
+    def forward(q_, k_, v_):
+        o = np.zeros((nq, hq, d))
+        lse = np.zeros((nq, hq))
+        for i in range(nq):
+            for h in range(hq):
+                js = [j for j in range(nk) if kp[j] <= qp[i]]
+                e = [math.exp(scale * sum(q_[i, h, t] * k_[j, 0, t] for t in range(d))) for j in js]
+                z = math.fsum(e)
+                lse[i, h] = math.log(z)
+                for t in range(d):
+                    o[i, h, t] = math.fsum(ej * v_[j, 0, t] for ej, j in zip(e, js)) / z
+        return o, lse
+
+    def loss(q_, k_, v_):
+        return math.fsum((forward(q_, k_, v_)[0] * do).ravel())
+
+    o, lse = forward(q, k, v)
+    delta = (o * do).sum(-1)
+    grads = bwd(q, k, v, do, lse, delta, qp, kp, True, scale)
+    eps = 1e-6
+    for x, g in zip((q, k, v), grads):
+        for idx in itertools.product(*(range(n) for n in x.shape)):
+            x0 = x[idx]
+            x[idx] = x0 + eps
+            lp = loss(q, k, v)
+            x[idx] = x0 - eps
+            lm = loss(q, k, v)
+            x[idx] = x0
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - g[idx]) < 1e-7 * max(1.0, abs(fd)), f"finite difference mismatch at {idx}"
+
+
+def check_bwd_zero_query(bwd, n=7, d=5, seed=22):
+    """Q = 0, no mask: P = 1/n everywhere, so dV_j = mean_i dO_i, dK = 0 and
+    dQ_i = (scale / n) sum_j <dO_i, v_j - mean v> k_j (closed forms)."""
+    r = _rng(seed)
+    q = np.zeros((n, 1, d))
+    k, v, do = (r.standard_normal((n, 1, d)) for _ in range(3))
+    scale = 0.9
+    lse = np.full((n, 1), math.log(n))
+    vbar = v[:, 0].mean(axis=0)
+    delta = (do[:, 0] @ vbar)[:, None]
+    dq, dk, dv = bwd(q, k, v, do, lse, delta, np.arange(n), np.arange(n), False, scale)
+    assert np.allclose(dv[:, 0], np.broadcast_to(do[:, 0].mean(axis=0), (n, d)), atol=1e-13), \
+        "Q=0: dV != mean of dO"
+    assert np.allclose(dk, 0.0, atol=1e-14), "Q=0: dK != 0"
+    want = (scale / n) * ((do[:, 0] @ (v[:, 0] - vbar).T) @ k[:, 0])
+    assert np.allclose(dq[:, 0], want, atol=1e-13), "Q=0: dQ closed form"
+
+
+def check_bwd_tile_sum(tile_bwd, tile_sets, R, C, causal=True, rot=True, L=3, hq=2, hkv=1, d=4,
+                       seed=23):
+    """The gradient shares of all tiles of an R x C mesh add up to the
+    gradient of full attention (torch autograd); each tile is given the
+    rows' full lse and D."""
+    r = _rng(seed)
+    P = R * C
+    N = P * L
+    q, do = (r.standard_normal((N, hq, d)) for _ in range(2))
+    k, v = (r.standard_normal((N, hkv, d)) for _ in range(2))
+    scale = 0.5
+    pos = np.arange(N)
+    rdq, rdk, rdv, lse, delta = _torch_full_grads(q, k, v, do, pos, pos, causal, scale)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for rr in range(R):
+        for cc in range(C):
+            q_parts, kv_parts = tile_sets(R, C, rr, cc, rot)
+            qi = _positions(q_parts, L)
+            ki = _positions(kv_parts, L)
+            a, b, c = tile_bwd(q[qi], k[ki], v[ki], do[qi], lse[qi], delta[qi], q_parts, kv_parts,
+                               L, causal, scale)
+            np.add.at(dq, qi, a)
+            np.add.at(dk, ki, b)
+            np.add.at(dv, ki, c)
+    for name, a, b in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        assert np.allclose(a, b, rtol=1e-10, atol=1e-11), f"tile shares of {name} do not sum to the gradient"
+
+
+def check_bwd_empty_rows(bwd, seed=24):
+    """Rows with lse = -inf (no visible key anywhere) contribute nothing."""
+    r = _rng(seed)
+    q, do = (r.standard_normal((4, 1, 3)) for _ in range(2))
+    k, v = (r.standard_normal((4, 1, 3)) for _ in range(2))
+    lse = np.full((4, 1), -np.inf)
+    dq, dk, dv = bwd(q, k, v, do, lse, np.zeros((4, 1)), np.arange(4), np.arange(4), False, 0.5)
+    assert np.all(dq == 0) and np.all(dk == 0) and np.all(dv == 0), "empty rows contributed"

@@ -107,6 +107,41 @@ BLOCK_MUTANTS = {
 }
 
 
+BW = oracle.attention_bwd_ref
+
+
+def _bwd_per_head_mod(q, k, v, do, lse, delta, qp, kp, c, s):
+    hq, hkv = q.shape[1], k.shape[1]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for h in range(hq):
+        hk = h % hkv
+        a, b, cc = BW(q[:, h:h + 1], k[:, hk:hk + 1], v[:, hk:hk + 1], do[:, h:h + 1], lse[:, h:h + 1],
+                      delta[:, h:h + 1], qp, kp, c, s)
+        dq[:, h:h + 1] += a
+        dk[:, hk:hk + 1] += b
+        dv[:, hk:hk + 1] += cc
+    return dq, dk, dv
+
+
+def _bwd_dk_unscaled(*a):
+    dq, dk, dv = BW(*a)
+    return dq, dk / a[-1], dv
+
+
+BWD_MUTANTS = {
+    "delta dropped": lambda q, k, v, do, l, dl, qp, kp, c, s: BW(q, k, v, do, l, 0 * dl, qp, kp, c, s),
+    "lse shifted": lambda q, k, v, do, l, dl, qp, kp, c, s: BW(q, k, v, do, l + 1e-6, dl, qp, kp, c, s),
+    "causal excludes self": lambda q, k, v, do, l, dl, qp, kp, c, s:
+        BW(q, k, v, do, l, dl, qp, np.asarray(kp) + 1, c, s),
+    "k and v swapped": lambda q, k, v, do, l, dl, qp, kp, c, s: BW(q, v, k, do, l, dl, qp, kp, c, s),
+    "dS sign flipped": lambda *a: (lambda r: (-r[0], -r[1], r[2]))(BW(*a)),
+    "dK without the scale": _bwd_dk_unscaled,
+    "head h % Hkv": _bwd_per_head_mod,
+    "dO taken as O's gradient twice": lambda q, k, v, do, l, dl, qp, kp, c, s:
+        BW(q, k, v, 2 * do, l, dl, qp, kp, c, s),
+}
+
+
 def _attention_checks(att):
     yield lambda: pins.check_sdpa(att, False)
     yield lambda: pins.check_sdpa(att, True)
@@ -130,6 +165,14 @@ def _block_checks(bl):
     for R, C in [(4, 4), (3, 5), (2, 3)]:
         yield lambda R=R, C=C: pins.check_block_list_geometry(bl, R, C)
         yield lambda R=R, C=C: pins.check_block_list_kinds(bl, R, C)
+
+
+def _bwd_checks(bw):
+    yield lambda: pins.check_bwd_autograd(bw, False)
+    yield lambda: pins.check_bwd_autograd(bw, True)
+    yield lambda: pins.check_bwd_finite_differences(bw)
+    yield lambda: pins.check_bwd_zero_query(bw)
+    yield lambda: pins.check_bwd_empty_rows(bw)
 
 
 def _caught(checks):
@@ -158,7 +201,13 @@ def test_block_list_mutant_is_caught(name):
     assert _caught(_block_checks(BLOCK_MUTANTS[name])) > 0, name
 
 
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_mutant_is_caught(name):
+    assert _caught(_bwd_checks(BWD_MUTANTS[name])) > 0, name
+
+
 def test_real_oracle_passes_every_check():
     assert _caught(_attention_checks(A)) == 0
     assert _caught(_merge_checks(oracle.lse_merge_ref)) == 0
     assert _caught(_block_checks(oracle.block_list_ref)) == 0
+    assert _caught(_bwd_checks(BW)) == 0

@@ -167,6 +167,47 @@ MESH_ATTN_API int mesh_attn_lse_merge(int32_t n_parts, int64_t rows, int32_t hea
                         const void *o_parts, const float *lse_parts, void *o_out,
                         float *lse_out, void *hip_stream);
 
+/*
+ * mesh_attn_bwd_delta - per-row D = sum_d dout * o, the term the attention
+ * backward subtracts in dS = P (dP - D).  The pages aim the method at
+ * long-context training (tutorial page, the greedy-scheduling section and
+ * the closing summary) but give no backward formula; this library takes the
+ * plain derivative of softmax attention.
+ *
+ *   o, dout [rows, head_dim] (dtype)      delta [rows] float32
+ *
+ * o is the rows' final (merged) output.  rows >= 0 (0 launches nothing);
+ * head_dim a multiple of 8 (bf16) or 4 (f32) between 8 and 512.  The dot
+ * product is accumulated in float32.
+ */
+MESH_ATTN_API int mesh_attn_bwd_delta(int64_t rows, int32_t head_dim, int32_t dtype, const void *o,
+                        const void *dout, float *delta, void *hip_stream);
+
+/*
+ * mesh_attn_tile_bwd - one tile's share of the attention gradients (same
+ * tile description and visibility rules as mesh_attn_tile_fwd).  For every
+ * visible pair of query row i (token, head h) and key j (KV head h / G) with
+ * s_ij = softmax_scale * q_i.k_j:
+ *   P_ij = exp(s_ij - lse_i)           lse_i: the row's final lse, natural log
+ *   dv_j += P_ij dout_i
+ *   dS_ij = P_ij (dout_i.v_j - delta_i)
+ *   dq_i += softmax_scale dS_ij k_j,   dk_j += softmax_scale dS_ij q_i
+ * Summed over all tiles of the mesh these are the gradients of full
+ * attention; a Q (KV) owner adds the dq (dk, dv) shares its peers return.
+ * A row with lse = -inf contributes nothing.
+ *
+ *   q, dout [n_q_slots*L, H_q, d] (dtype)   lse, delta [n_q_slots*L, H_q] float32
+ *   k, v    [n_kv_slots*L, H_kv, d] (dtype)
+ *   dq      [n_q_slots*L, H_q, d] float32   (written, not accumulated)
+ *   dk, dv  [n_kv_slots*L, H_kv, d] float32 (written, not accumulated)
+ * Rows of dq, dk and dv that no visible pair reaches are written as 0.
+ * Validation as for mesh_attn_tile_fwd (messages say "tile_bwd"); built for
+ * bf16 with d = 128, anything else returns MESH_ATTN_ERR_UNSUPPORTED.
+ */
+MESH_ATTN_API int mesh_attn_tile_bwd(const mesh_attn_tile_desc *desc, const void *q, const void *k,
+                       const void *v, const void *dout, const float *lse, const float *delta,
+                       float *dq, float *dk, float *dv, void *hip_stream);
+
 /* Text of a status code (static storage). */
 MESH_ATTN_API const char *mesh_attn_status_string(int status);
 

@@ -7,6 +7,8 @@ every step of the computation runs in the library's HIP kernels.
     block_list(mesh_rows, mesh_cols, row, col, causal, kv_rotate) -> [Block tuples]
     tile_fwd(q, k, v, blocks, part_len, softmax_scale=None) -> (o, lse)
     lse_merge(o_parts, lse_parts) -> (o, lse)
+    bwd_delta(o, dout) -> delta
+    tile_bwd(q, k, v, dout, lse, delta, blocks, part_len, softmax_scale=None) -> (dq, dk, dv)
 """
 import ctypes
 import math
@@ -14,8 +16,8 @@ import math
 from . import _lib
 from ._lib import BF16, DIAG, F32, FULL, SKIP  # noqa: F401
 
-__all__ = ["MeshAttnError", "block_list", "tile_fwd", "lse_merge", "FULL", "DIAG", "SKIP",
-           "library_path"]
+__all__ = ["MeshAttnError", "block_list", "tile_fwd", "lse_merge", "bwd_delta", "tile_bwd",
+           "FULL", "DIAG", "SKIP", "library_path"]
 
 
 class MeshAttnError(RuntimeError):
@@ -73,16 +75,7 @@ def _require_device(*ts):
             raise ValueError("tensors must be contiguous")
 
 
-def tile_fwd(q, k, v, blocks, part_len, softmax_scale=None, out=None, lse=None, stream=None):
-    """Forward of one tile.
-
-    q: [n_q_slots*L, H_q, d], k/v: [n_kv_slots*L, H_kv, d] on the device
-    (bf16 or f32, same dtype); blocks: iterable of (q_slot, kv_slot, q_part,
-    kv_part, kind).  Returns (o [n_q_slots*L, H_q, d], lse [n_q_slots*L, H_q]
-    float32), allocated with torch unless given.
-    """
-    import torch
-    lib = _lib.load()
+def _tile_desc(q, k, v, blocks, part_len, softmax_scale):
     _require_device(q, k, v)
     if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
         raise ValueError("expected q [Tq, Hq, d] and k, v [Tk, Hkv, d]")
@@ -101,6 +94,22 @@ def tile_fwd(q, k, v, blocks, part_len, softmax_scale=None, out=None, lse=None, 
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     desc = _lib.TileDesc(_dtype_code(q), part_len, tq // part_len, tk // part_len, hq, hkv, d,
                          scale, arr, len(blocks))
+    desc._keep = arr  # the block array must outlive the call
+    return desc
+
+
+def tile_fwd(q, k, v, blocks, part_len, softmax_scale=None, out=None, lse=None, stream=None):
+    """Forward of one tile.
+
+    q: [n_q_slots*L, H_q, d], k/v: [n_kv_slots*L, H_kv, d] on the device
+    (bf16 or f32, same dtype); blocks: iterable of (q_slot, kv_slot, q_part,
+    kv_part, kind).  Returns (o [n_q_slots*L, H_q, d], lse [n_q_slots*L, H_q]
+    float32), allocated with torch unless given.
+    """
+    import torch
+    lib = _lib.load()
+    desc = _tile_desc(q, k, v, blocks, part_len, softmax_scale)
+    tq, hq = q.shape[0], q.shape[1]
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -138,3 +147,59 @@ def lse_merge(o_parts, lse_parts, out=None, lse_out=None, want_lse=True, stream=
                                         lse_out.data_ptr() if lse_out is not None else None,
                                         _stream_handle(stream, o_parts.device)))
     return out, lse_out
+
+
+def bwd_delta(o, dout, out=None, stream=None):
+    """D = sum over the last dimension of dout * o, float32: o, dout [..., d]
+    (bf16 or f32, same shape) -> delta [...]."""
+    import torch
+    lib = _lib.load()
+    _require_device(o, dout)
+    if o.shape != dout.shape or o.dtype != dout.dtype:
+        raise ValueError("o and dout must share shape and dtype")
+    d = o.shape[-1]
+    rows = o.numel() // d if d else 0
+    if out is None:
+        out = torch.empty(o.shape[:-1], dtype=torch.float32, device=o.device)
+    _require_device(out)
+    if out.shape != o.shape[:-1] or out.dtype != torch.float32:
+        raise ValueError("output buffer has the wrong shape or dtype")
+    _check(lib, lib.mesh_attn_bwd_delta(rows, d, _dtype_code(o), o.data_ptr(), dout.data_ptr(),
+                                        out.data_ptr(), _stream_handle(stream, o.device)))
+    return out
+
+
+def tile_bwd(q, k, v, dout, lse, delta, blocks, part_len, softmax_scale=None, dq=None, dk=None,
+             dv=None, stream=None):
+    """One tile's share of the attention gradients.
+
+    q, dout: [n_q_slots*L, H_q, d]; k, v: [n_kv_slots*L, H_kv, d] (bf16);
+    lse, delta: [n_q_slots*L, H_q] float32 (the rows' final lse and
+    rowsum(dout * o)).  Returns (dq, dk, dv) in float32, allocated with torch
+    unless given.
+    """
+    import torch
+    lib = _lib.load()
+    desc = _tile_desc(q, k, v, blocks, part_len, softmax_scale)
+    _require_device(dout, lse, delta)
+    tq, hq = q.shape[0], q.shape[1]
+    if dout.shape != q.shape or dout.dtype != q.dtype:
+        raise ValueError("dout must match q")
+    if lse.shape != (tq, hq) or delta.shape != (tq, hq) or lse.dtype != torch.float32 or \
+            delta.dtype != torch.float32:
+        raise ValueError("lse and delta must be float32 [Tq, Hq]")
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    _require_device(dq, dk, dv)
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape or \
+            any(t.dtype != torch.float32 for t in (dq, dk, dv)):
+        raise ValueError("gradient buffers have the wrong shape or dtype")
+    _check(lib, lib.mesh_attn_tile_bwd(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                       dout.data_ptr(), lse.data_ptr(), delta.data_ptr(),
+                                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                       _stream_handle(stream, q.device)))
+    return dq, dk, dv

@@ -28,6 +28,7 @@ MAX_BLOCKS = 1024
 
 # Every symbol include/mesh_attn.h declares.
 EXPORTS = ("mesh_attn_block_list", "mesh_attn_tile_fwd", "mesh_attn_lse_merge",
+           "mesh_attn_bwd_delta", "mesh_attn_tile_bwd",
            "mesh_attn_status_string", "mesh_attn_last_error", "mesh_attn_version")
 
 
@@ -67,6 +68,10 @@ def load():
     lib.mesh_attn_tile_fwd.restype = ctypes.c_int
     lib.mesh_attn_lse_merge.argtypes = [i32, i64, i32, i32, vp, vp, vp, vp, vp]
     lib.mesh_attn_lse_merge.restype = ctypes.c_int
+    lib.mesh_attn_bwd_delta.argtypes = [i64, i32, i32, vp, vp, vp, vp]
+    lib.mesh_attn_bwd_delta.restype = ctypes.c_int
+    lib.mesh_attn_tile_bwd.argtypes = [ctypes.POINTER(TileDesc)] + [vp] * 10
+    lib.mesh_attn_tile_bwd.restype = ctypes.c_int
     lib.mesh_attn_status_string.argtypes = [ctypes.c_int]
     lib.mesh_attn_status_string.restype = ctypes.c_char_p
     lib.mesh_attn_last_error.argtypes = []

@@ -53,7 +53,7 @@ struct TileParams {
     int32_t group;         // G = H_q / H_kv
     int32_t heads_per_wg;  // query heads of one KV group handled by a workgroup
     int32_t tok_groups;    // token row groups per workgroup (waves / heads_per_wg)
-    int32_t wave_rows;     // query rows (tokens) per wave: 64 for bf16, 32 for f32
+    int32_t wave_rows;     // query rows (tokens) per wave
     int32_t n_tok_blocks;  // ceil(L / (wave_rows * tok_groups))
     int32_t n_head_groups; // G / heads_per_wg
     int32_t n_q_slots;
@@ -69,8 +69,80 @@ constexpr int kTileWavesF32 = 4;
 constexpr int kWaveRowsBf16 = 32;
 constexpr int kWaveRowsF32 = 32;
 
+// The same blocks seen from the KV side, for the key/value-gradient kernel:
+// for KV slot j the entries blk[blk_off[j] .. blk_off[j+1]) are
+// (q_slot << 2) | kind, non-SKIP blocks only, in Q-slot order.
+struct KvSchedule {
+    uint8_t blk[kMaxBlocks];
+    uint16_t blk_off[kMaxKvSlots + 2];
+};
+
+static_assert(sizeof(KvSchedule) % 4 == 0, "schedule size");
+
+// Arguments of the query-gradient kernel: Q-stationary, with the same work
+// decomposition (and fields) as the forward.
+struct BwdDqParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;
+    const float* lse;
+    const float* delta;
+    float* dq;
+    int32_t part_len;
+    int32_t heads_q;
+    int32_t heads_kv;
+    int32_t group;
+    int32_t heads_per_wg;
+    int32_t tok_groups;
+    int32_t wave_rows;
+    int32_t n_tok_blocks;
+    int32_t n_head_groups;
+    int32_t n_q_slots;
+    float scale;           // softmax_scale
+    float scale_log2e;     // softmax_scale * log2(e)
+    TileSchedule sched;
+};
+
+static_assert(offsetof(BwdDqParams, sched) % 4 == 0, "schedule must be dword aligned");
+
+// Arguments of the key/value-gradient kernel: KV-stationary.  The grid is
+// (KV slot, key block, KV head) with the KV head varying fastest.
+struct BwdDkvParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;
+    const float* lse;
+    const float* delta;
+    float* dk;
+    float* dv;
+    int32_t part_len;
+    int32_t heads_q;
+    int32_t heads_kv;
+    int32_t group;
+    int32_t n_kv_slots;
+    int32_t n_key_blocks;  // ceil(L / keys per workgroup)
+    float scale;
+    float scale_log2e;
+    KvSchedule sched;
+};
+
+static_assert(offsetof(BwdDkvParams, sched) % 4 == 0, "schedule must be dword aligned");
+
+// Waves per workgroup of the backward kernels; every wave owns 32 query rows
+// (query-gradient kernel) or 32 keys (key/value-gradient kernel).
+constexpr int kBwdDqWaves = 8;
+constexpr int kBwdDkvWaves = 8;
+constexpr int kBwdRowsPerWave = 32;
+
 hipError_t launch_tile_fwd_bf16(const TileParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_tile_fwd_f32(const TileParams& p, int head_dim, hipStream_t stream);
+
+hipError_t launch_tile_bwd_bf16(const BwdDqParams& pq, const BwdDkvParams& pk, int head_dim,
+                               hipStream_t stream);
+hipError_t launch_bwd_delta(int64_t rows, int head_dim, int dtype, const void* o, const void* dout,
+                            float* delta, hipStream_t stream);
 
 hipError_t launch_lse_merge(int n_parts, int64_t rows, int head_dim, int dtype,
                             const void* o_parts, const float* lse_parts, void* o_out,

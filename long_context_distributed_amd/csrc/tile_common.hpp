@@ -47,7 +47,10 @@ struct WorkItem {
 // blockIdx.x -> work item.  KV head varies fastest, then query-head group,
 // then token block (highest first: in a DIAG block later tokens see more
 // keys), then Q slot in heaviest-first order.
-__device__ __forceinline__ WorkItem decode_work(const TileParams& p, int wave) {
+// Works for every parameter struct with the forward's decomposition fields
+// (TileParams, BwdDqParams).
+template <typename Params>
+__device__ __forceinline__ WorkItem decode_work(const Params& p, int wave) {
     int lam = blockIdx.x;
     WorkItem w;
     w.kv_head = lam % p.heads_kv;

@@ -25,6 +25,12 @@ hipError_t launch_tile_fwd_bf16(const TileParams&, int, hipStream_t) { return hi
 hipError_t launch_tile_fwd_f32(const TileParams&, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_lse_merge(int, int64_t, int, int, const void*, const float*, void*, float*,
                             hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_tile_bwd_bf16(const BwdDqParams&, const BwdDkvParams&, int, hipStream_t) {
+    return hipErrorNoDevice;
+}
+hipError_t launch_bwd_delta(int64_t, int, int, const void*, const void*, float*, hipStream_t) {
+    return hipErrorNoDevice;
+}
 }
 """
 
@@ -56,6 +62,10 @@ DRIVER = textwrap.dedent("""
             st = lib.mesh_attn_tile_fwd(ctypes.byref(desc(bl, dtype=dtype, nq=C, nkv=R, d=d)),
                                         FAKE, FAKE, FAKE, FAKE, FAKE, None)
             assert st == _lib.ERR_HIP, st
+        st = lib.mesh_attn_tile_bwd(ctypes.byref(desc(bl, nq=C, nkv=R)), *([FAKE] * 9), None)
+        assert st == _lib.ERR_HIP, st
+        assert lib.mesh_attn_tile_bwd(ctypes.byref(desc(bl, dtype=1, nq=C, nkv=R)), *([FAKE] * 9),
+                                      None) == _lib.ERR_UNSUPPORTED
     # every invalid descriptor is rejected
     bl = oracle.block_list_ref(2, 2, 0, 0, True, True)
     for kw in (dict(dtype=7), dict(L=0), dict(nq=0), dict(nq=65), dict(hq=3), dict(scale=0.0),
@@ -69,6 +79,8 @@ DRIVER = textwrap.dedent("""
                                   FAKE, None) == _lib.ERR_HIP
     assert lib.mesh_attn_lse_merge(8, 1 << 20, 128, 0, FAKE, FAKE, FAKE, FAKE, None) == _lib.ERR_HIP
     assert lib.mesh_attn_lse_merge(0, 16, 128, 0, FAKE, FAKE, FAKE, FAKE, None) == _lib.ERR_INVALID
+    assert lib.mesh_attn_bwd_delta(1 << 20, 128, 0, FAKE, FAKE, FAKE, None) == _lib.ERR_HIP
+    assert lib.mesh_attn_bwd_delta(16, 12, 0, FAKE, FAKE, FAKE, None) == _lib.ERR_INVALID
     print("sanitized host path ok")
 """)
 

@@ -193,3 +193,47 @@ def test_merge_invalid(lib, kw):
 
 def test_merge_zero_rows_is_a_noop(lib):
     assert _merge(lib, rows=0) == _lib.OK
+
+
+# ----------------------------------------------------------------------------- backward
+
+def _bwd(lib, desc, by_ref=True, **ptrs):
+    names = ("q", "k", "v", "dout", "lse", "delta", "dq", "dk", "dv")
+    args = [ptrs.get(n, FAKE) for n in names]
+    return lib.mesh_attn_tile_bwd(ctypes.byref(desc) if by_ref else None, *args, None)
+
+
+@pytest.mark.parametrize("name", sorted(INVALID_DESCS))
+def test_tile_bwd_invalid_desc(lib, name):
+    assert _bwd(lib, _desc(**INVALID_DESCS[name])) == _lib.ERR_INVALID
+    assert lib.mesh_attn_last_error().startswith(b"tile_bwd")
+
+
+@pytest.mark.parametrize("name", sorted(_bad_blocks()))
+def test_tile_bwd_invalid_blocks(lib, name):
+    assert _bwd(lib, _desc(blocks=_bad_blocks()[name])) == _lib.ERR_INVALID
+
+
+def test_tile_bwd_null_misaligned_unsupported(lib):
+    d = _desc()
+    assert _bwd(lib, d, by_ref=False) == _lib.ERR_INVALID
+    for field in ("q", "k", "v", "dout", "lse", "delta", "dq", "dk", "dv"):
+        assert _bwd(lib, d, **{field: None}) == _lib.ERR_INVALID
+        assert _bwd(lib, d, **{field: FAKE + 4}) == _lib.ERR_INVALID
+    assert _bwd(lib, _desc(head_dim=64)) == _lib.ERR_UNSUPPORTED
+    assert _bwd(lib, _desc(dtype=_lib.F32)) == _lib.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(rows=-1), dict(dtype=5), dict(d=0), dict(d=12), dict(d=1024),
+                                dict(dtype=_lib.F32, d=6), dict(o=None), dict(do=None),
+                                dict(out=None), dict(o=FAKE + 8), dict(do=FAKE + 8),
+                                dict(out=FAKE + 2), dict(rows=1 << 62)])
+def test_bwd_delta_invalid(lib, kw):
+    a = dict(rows=16, d=128, dtype=_lib.BF16, o=FAKE, do=FAKE, out=FAKE)
+    a.update(kw)
+    assert lib.mesh_attn_bwd_delta(a["rows"], a["d"], a["dtype"], a["o"], a["do"], a["out"],
+                                   None) == _lib.ERR_INVALID
+
+
+def test_bwd_delta_zero_rows_is_a_noop(lib):
+    assert lib.mesh_attn_bwd_delta(0, 128, _lib.BF16, FAKE, FAKE, FAKE, None) == _lib.OK

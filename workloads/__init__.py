@@ -8,14 +8,15 @@ side, the oracle's on the checking side); this module just draws and
 concatenates them.
 
 Every (tensor, partition) pair has its own random stream, so two sibling
-tiles that hold the same partition see identical values.
+tiles that hold the same partition see identical values.  "do" is the
+gradient of the attention output for the backward (shaped like q).
 """
 
 from dataclasses import dataclass
 
 import numpy as np
 
-TENSORS = ("q", "k", "v")
+TENSORS = ("q", "k", "v", "do")
 
 
 @dataclass(frozen=True)
@@ -33,7 +34,7 @@ class Workload:
     heads_q: int
     heads_kv: int
     head_dim: int
-    std: tuple = (1.0, 1.0, 1.0)  # standard deviation of q, k, v
+    std: tuple = (1.0, 1.0, 1.0)  # standard deviation of q, k, v (do: 1)
     seed: int = 0
     merge: str = "siblings"  # "siblings" or "per_kv_part"
     numpy_whole_sequence: bool = False  # draw Q, K, V of the whole sequence with numpy
@@ -71,16 +72,18 @@ def stream_seed(seed, tensor, part):
 
 
 def _std(w, tensor):
-    return float(w.std[TENSORS.index(tensor)])
+    i = TENSORS.index(tensor)
+    return float(w.std[i]) if i < len(w.std) else 1.0
 
 
 def _heads(w, tensor):
-    return w.heads_q if tensor == "q" else w.heads_kv
+    return w.heads_q if tensor in ("q", "do") else w.heads_kv
 
 
 def _numpy_sequence(w):
     """Whole-sequence draw for the fp32 workload: numpy default_rng(seed)
-    produces Q, K, V in that order as float64 standard normals, cast to fp32."""
+    produces Q, K, V (then dO) in that order as float64 standard normals, cast
+    to fp32."""
     rng = np.random.default_rng(w.seed)
     out = {}
     for t in TENSORS:

@@ -12,7 +12,13 @@ are dead.  Their correctness against real sibling tiles is what the parity
 tests check.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
-                    [--no-cpu-baseline] [--copy-calibration MIB]
+                    [--backward-steps N] [--no-cpu-baseline] [--copy-calibration MIB]
+
+After the forward steps, --backward-steps N (default 3, 0 = off; bf16 tiles)
+times the tile backward on the same tile: the row-term kernel D = rowsum(dO*O)
+and the dQ and dK/dV kernels, reported in "tile_bwd" (not part of "value").
+The rows' lse and O are this tile's own forward results, which have the shapes
+and value ranges of the final ones; dO is synthetic.
 
 --copy-calibration runs one plain device copy of MIB MiB after the steps, so
 that a hardware-counter run can scale FETCH_SIZE / WRITE_SIZE by what they
@@ -39,6 +45,8 @@ PEAK_HBM_GBS = 8000.0
 # Kernel sources whose hash keys the counter-derived traffic in profiles/.
 KERNEL_SOURCES = {
     "tile_fwd_bf16_d128": ["tile_fwd_bf16.hip", "tile_common.hpp", "kernels.h"],
+    "tile_bwd_dq_bf16_d128": ["tile_bwd_bf16.hip", "tile_common.hpp", "kernels.h"],
+    "tile_bwd_dkdv_bf16_d128": ["tile_bwd_bf16.hip", "tile_common.hpp", "kernels.h"],
     "tile_fwd_f32": ["tile_fwd_f32.hip", "tile_common.hpp", "kernels.h"],
     "lse_merge_kernel": ["lse_merge.hip", "kernels.h"],
 }
@@ -131,12 +139,70 @@ def cpu_baseline(w, q, k, v, q_parts, kv_parts, budget_s=12.0):
                       f"softmax over their visible keys, {t_used:.1f} s"}
 
 
+def backward_leg(steps, w, q, k, v, o, lse, q_parts, blocks, fwd_flops, dev):
+    """Times the tile backward: D = rowsum(dO * O), then dQ and dK/dV."""
+    import torch
+    import long_context_distributed_amd as mat
+    import workloads
+    do = workloads.gather(w, "do", q_parts, dev)
+    delta = torch.empty_like(lse)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(w.head_dim)
+
+    def run(ev):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if ev is not None else None
+        if e:
+            e[0].record()
+        mat.bwd_delta(o, do, out=delta)
+        if e:
+            e[1].record()
+        mat.tile_bwd(q, k, v, do, lse, delta, blocks, w.part_len, scale, dq=dq, dk=dk, dv=dv)
+        if e:
+            e[2].record()
+            ev.append(e)
+
+    run(None)
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(steps):
+        run(ev)
+    torch.cuda.synchronize()
+    t_delta = sum(e[0].elapsed_time(e[1]) for e in ev) / len(ev)
+    t_bwd = sum(e[1].elapsed_time(e[2]) for e in ev) / len(ev)
+    bwd_flops = 2.5 * fwd_flops        # five products of 2*d flops per visible pair and head
+    exec_flops = 3.5 * fwd_flops       # seven: S and dP are formed in both kernels
+    tflops = bwd_flops / (t_bwd * 1e-3) / 1e12
+    dbytes = 2 * o.numel() * o.element_size() + delta.numel() * 4
+    log(f"[bench] backward {t_bwd:.3f} ms = {tflops:.1f} TFLOP/s algorithmic "
+        f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak), "
+        f"{exec_flops / (t_bwd * 1e-3) / 1e12:.1f} TFLOP/s executed; row terms {t_delta:.3f} ms")
+    return {"ms": t_bwd, "tflops": tflops, "frac_peak": tflops / PEAK_BF16_TFLOPS,
+            "flops": bwd_flops, "executed_flops": exec_flops,
+            "executed_tflops": exec_flops / (t_bwd * 1e-3) / 1e12, "steps": steps,
+            "kernels": ["tile_bwd_dq_bf16_d128", "tile_bwd_dkdv_bf16_d128"],
+            "traffic": {kn: measured_traffic(kn, w_id(w)) for kn in
+                        ("tile_bwd_dq_bf16_d128", "tile_bwd_dkdv_bf16_d128")},
+            "row_terms": {"ms": t_delta, "bytes": dbytes,
+                          "gbs": dbytes / (t_delta * 1e-3) / 1e9}}
+
+
+def w_id(w):
+    import workloads
+    for i, x in workloads.WORKLOADS.items():
+        if x is w:
+            return i
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--backward-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
@@ -269,6 +335,9 @@ def main():
                      "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE)",
                      "kernel": tile_kernel},
     }
+    if a.backward_steps > 0 and w.dtype == "bf16":
+        result["tile_bwd"] = backward_leg(a.backward_steps, w, q, k, v, o_own, l_own, q_parts,
+                                          blocks, flops, dev)
     if a.copy_calibration > 0:
         src = torch.empty(a.copy_calibration << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -14,10 +14,11 @@
 //                  streaming; per 32 keys it recomputes S^T = K Q^T and
 //                  dP^T = V dO^T and accumulates dQ^T += K^T dS^T.
 //   tile_bwd_dkdv: KV-stationary; a workgroup owns 256 keys of one KV head
-//                  (32 per wave) and streams the query rows of every Q slot
-//                  that sees them, all query heads of the group; per 32 rows
-//                  it computes S = Q K^T and dP = dO V^T and accumulates
-//                  dV^T += dO^T P and dK^T += Q^T dS.
+//                  (32 per wave; K in LDS, V in registers) and streams the
+//                  query rows of every Q slot that sees them, 64 rows of one
+//                  query head per stage (DMA into two LDS stages, one barrier
+//                  per stage); per 32 rows it computes S = Q K^T and
+//                  dP = dO V^T and accumulates dV^T += dO^T P and dK^T += Q^T dS.
 // Each recomputes what the other needs (7 matrix products per pair instead
 // of the 5 of the gradient formulas).
 //
@@ -332,13 +333,17 @@ __global__ __launch_bounds__(QT, 1) void tile_bwd_dq_bf16_d128(const BwdDqParams
 constexpr int KW = kBwdDkvWaves;
 constexpr int KT = KW * 64;
 constexpr int KB = KW * kBwdRowsPerWave;        // keys per workgroup
-constexpr int kRows = 32;                       // query rows per stage
-constexpr int kStageTile = kRows * kRowBytes;   // 8 KiB of Q or dO
-constexpr int kStageBytes = 2 * kStageTile + 2 * kRows * 4;  // Q, dO, -lse/scale, -D
+constexpr int kRows = 64;                       // query rows per stage (two 32-row blocks)
+constexpr int kStageTile = kRows * kRowBytes;   // 16 KiB of Q or dO
+constexpr int kTermOff = 2 * kStageTile;        // then -lse/scale and -D, one float per row each
+constexpr int kStageBytes = kTermOff + 2 * kRows * 4;
 constexpr int kNStage = 2;
 constexpr int kKTileBytes = KB * kRowBytes;     // 64 KiB
-static_assert(kRows * 16 == KT, "one 16-byte chunk of Q and of dO per thread and stage");
+constexpr int kStageRegions = 2 * kStageTile / 1024;    // DMA loads per stage (Q then dO)
+constexpr int kStageDmaPerWave = kStageRegions / KW;
+static_assert(kStageRegions % KW == 0, "stage DMA loads split evenly over the waves");
 static_assert(KB * 16 % KT == 0, "K tile chunks split evenly over the threads");
+static_assert(kRows == 64, "row terms are written by one wave, one lane per row");
 
 __device__ __forceinline__ int kv_entry(const KvSchedule& s, int i) {
     const uint32_t word = reinterpret_cast<const uint32_t*>(s.blk)[i >> 2];
@@ -369,10 +374,20 @@ __global__ __launch_bounds__(KT, 1) void tile_bwd_dkdv_bf16_d128(const BwdDkvPar
 
     LDS_AS unsigned char* lds = (LDS_AS unsigned char*)smem;
     LDS_AS unsigned char* ktile = lds;
-    LDS_AS unsigned char* stages = lds + kKTileBytes;
+    const unsigned stage0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(lds + kKTileBytes));
 
     TileOffsets to;
     init_offsets(to, lane);
+    // Stage DMA: load i of this wave fills region reg = wave + KW*i (Q rows
+    // 4*reg .. for reg < 16, dO rows 4*(reg-16) .. after), lane l to row
+    // 4*(reg%16) + l/16, physical chunk l%16.
+    int dma_gofs[kStageDmaPerWave];
+#pragma unroll
+    for (int i = 0; i < kStageDmaPerWave; ++i) {
+        const int reg = wave + KW * i;
+        const int row = 4 * (reg & 15) + (lane >> 4);
+        dma_gofs[i] = row * q_row_bytes + (((lane & 15) ^ swz(row)) << 4);
+    }
 
     // K tile of the workgroup's keys into LDS; V^T fragments (B operand of
     // dP = dO V^T: key r32 of this wave, dims 16c + 8g ..) into registers.
@@ -405,11 +420,11 @@ __global__ __launch_bounds__(KT, 1) void tile_bwd_dkdv_bf16_d128(const BwdDkvPar
             dv[t][i] = 0.0f;
         }
 
-    // Items: (entry e, row tile r0, head hh) with the head innermost.
+    // Items: (entry e, row tile r0 of 64 rows, head hh), head innermost.  A
+    // DIAG entry starts at row key0: earlier rows see none of these keys.
     const int e_beg = p.sched.blk_off[kv_slot];
     const int e_end = p.sched.blk_off[kv_slot + 1];
     auto first_row = [&](int e) { return (kv_entry(p.sched, e) & 3) == kDiag ? key0 : 0; };
-    // Skip entries with no rows (a DIAG block whose rows all precede key0 cannot occur: rows run to L > key0).
     int e = e_beg, r0 = e_beg < e_end ? first_row(e_beg) : 0, hh = 0;
     auto step_item = [&](int& e_, int& r0_, int& hh_) {
         if (++hh_ == G) {
@@ -422,98 +437,98 @@ __global__ __launch_bounds__(KT, 1) void tile_bwd_dkdv_bf16_d128(const BwdDkvPar
         }
     };
 
-    // Stage loader: thread tid holds chunk (row tid/16, chunk tid%16) of the
-    // Q and dO tiles; threads 0..31 the row terms of -lse/scale, 32..63 -D.
-    u32x4 qv, dov;
-    float term = 0.0f;
-    auto load_item = [&](int e_, int r0_, int hh_) {
+    // Issues the loads of item (e_, r0_, hh_) into stage st: Q and dO rows by
+    // DMA (rows at or past L read as zero), the row terms by wave 0 through
+    // registers (-lse/scale, -inf for rows that see nothing; -D).
+    auto load_item = [&](int e_, int r0_, int hh_, int st) {
         const int s = kv_entry(p.sched, e_) >> 2;
         const int h = kv_head * G + hh_;
         const size_t first = ((size_t)(s * L + r0_) * p.heads_q + h) * D;
-        const Rsrc qr = rows_rsrc(reinterpret_cast<const __bf16*>(p.q) + first, L - r0_, q_row_bytes);
-        const Rsrc dr = rows_rsrc(reinterpret_cast<const __bf16*>(p.dout) + first, L - r0_, q_row_bytes);
-        const int row = tid >> 4, c = tid & 15;
-        qv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, row * q_row_bytes + c * 16, 0, 0));
-        dov = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(dr, row * q_row_bytes + c * 16, 0, 0));
-        if (tid < 2 * kRows) {
-            const int rr = r0_ + (tid & (kRows - 1));
+        const u32x4 qd = rows_desc(reinterpret_cast<const __bf16*>(p.q) + first, L - r0_, q_row_bytes);
+        const u32x4 dd = rows_desc(reinterpret_cast<const __bf16*>(p.dout) + first, L - r0_, q_row_bytes);
+        const unsigned dst = stage0 + st * kStageBytes;
+#pragma unroll
+        for (int i = 0; i < kStageDmaPerWave; ++i) {
+            const int reg = wave + KW * i;
+            dma_1k(dst + reg * 1024, dma_gofs[i], reg < 16 ? qd : dd);
+        }
+        if (wave == 0) {
+            const int rr = r0_ + lane;
             const size_t qi = (size_t)(s * L + min(rr, L - 1)) * p.heads_q + h;
-            if (tid < kRows) {
-                const float ls = rr < L ? p.lse[qi] : kNegInf;
-                term = ls > kNegInf ? ls * neg_inv_scale : kNegInf;
-            } else {
-                term = rr < L ? -p.delta[qi] : 0.0f;
-            }
+            const float ls = rr < L ? p.lse[qi] : kNegInf;
+            const float dl = rr < L ? p.delta[qi] : 0.0f;
+            LDS_AS float* terms = reinterpret_cast<LDS_AS float*>(lds + kKTileBytes + st * kStageBytes + kTermOff);
+            terms[lane] = ls > kNegInf ? ls * neg_inv_scale : kNegInf;
+            terms[kRows + lane] = -dl;
         }
     };
-    auto store_item = [&](int st) {
-        LDS_AS unsigned char* base = stages + st * kStageBytes;
-        const int row = tid >> 4, c = tid & 15;
-        const int off = row * kRowBytes + ((c ^ swz(row)) << 4);
-        *reinterpret_cast<LDS_AS u32x4*>(base + off) = qv;
-        *reinterpret_cast<LDS_AS u32x4*>(base + kStageTile + off) = dov;
-        if (tid < 2 * kRows) *reinterpret_cast<LDS_AS float*>(base + 2 * kStageTile + 4 * tid) = term;
+    auto vmcnt0_barrier = [&]() {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
     };
 
     const LDS_AS unsigned char* kw_tile = ktile + 32 * wave * kRowBytes;
     int st = 0;
-    if (e < e_end) {
-        load_item(e, r0, hh);
-        store_item(0);
-    }
-    __syncthreads();  // K tile and stage 0
+    if (e < e_end) load_item(e, r0, hh, 0);
+    vmcnt0_barrier();  // K tile and stage 0
 
     while (e < e_end) {
         int e1 = e, r01 = r0, hh1 = hh;
         step_item(e1, r01, hh1);
         const bool more = e1 < e_end;
-        if (more) load_item(e1, r01, hh1);  // in flight during the compute below
+        // The other stage was last read before the previous barrier.
+        if (more) load_item(e1, r01, hh1, st ^ 1);
 
-        const LDS_AS unsigned char* base = stages + st * kStageBytes;
+        const LDS_AS unsigned char* base = lds + kKTileBytes + st * kStageBytes;
         const bool dg = (kv_entry(p.sched, e) & 3) == kDiag;
-        // S = Q K^T - lse/scale and dP = dO V^T - D (row terms as initial values).
-        f32x16 s, dp;
 #pragma unroll
-        for (int ib = 0; ib < 4; ++ib) {
-            const f32x4 a = *reinterpret_cast<const LDS_AS f32x4*>(base + 2 * kStageTile + 4 * (8 * ib + 4 * g));
-            const f32x4 b = *reinterpret_cast<const LDS_AS f32x4*>(base + 2 * kStageTile + 4 * kRows + 4 * (8 * ib + 4 * g));
+        for (int sub = 0; sub < 2; ++sub) {
+            const int rs = r0 + 32 * sub;          // first row of this 32-row block
+            if (rs >= L) break;                    // uniform: past the partition
+            const LDS_AS unsigned char* qb = base + sub * 32 * kRowBytes;
+            const LDS_AS unsigned char* db = qb + kStageTile;
+            const LDS_AS unsigned char* tb = base + kTermOff + 4 * 32 * sub;
+            // S = Q K^T - lse/scale and dP = dO V^T - D (row terms as initial values).
+            f32x16 s, dp;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                s[4 * ib + j] = a[j];
-                dp[4 * ib + j] = b[j];
+            for (int ib = 0; ib < 4; ++ib) {
+                const f32x4 a = *reinterpret_cast<const LDS_AS f32x4*>(tb + 4 * (8 * ib + 4 * g));
+                const f32x4 b = *reinterpret_cast<const LDS_AS f32x4*>(tb + 4 * kRows + 4 * (8 * ib + 4 * g));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    s[4 * ib + j] = a[j];
+                    dp[4 * ib + j] = b[j];
+                }
             }
-        }
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_b128(base + to.row[c]), read_b128(kw_tile + to.row[c]), s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_b128(base + kStageTile + to.row[c]), vf[c], dp, 0, 0, 0);
-        }
-        if (kw0 + 31 >= L || (dg && kw0 + 31 > r0)) {
+            for (int c = 0; c < 8; ++c) {
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_b128(qb + to.row[c]), read_b128(kw_tile + to.row[c]), s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_b128(db + to.row[c]), vf[c], dp, 0, 0, 0);
+            }
+            if (kw0 + 31 >= L || (dg && kw0 + 31 > rs)) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int row = rs + 8 * (i >> 2) + 4 * g + (i & 3);
+                    if (key >= L || (dg && key > row)) s[i] = kNegInf;
+                }
+            }
+            bf16x8 pb[2], dsb[2];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int row = r0 + 8 * (i >> 2) + 4 * g + (i & 3);
-                if (key >= L || (dg && key > row)) s[i] = kNegInf;
+                const float pv = dev::fast_exp2(s[i] * c2);
+                pb[i >> 3][i & 7] = static_cast<__bf16>(pv);
+                dsb[i >> 3][i & 7] = static_cast<__bf16>(pv * dp[i]);
             }
+            // dV^T += dO^T P, dK^T += Q^T dS
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(to, db, t, kk), pb[kk], dv[t], 0, 0, 0);
+                    dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(to, qb, t, kk), dsb[kk], dk[t], 0, 0, 0);
+                }
         }
-        bf16x8 pb[2], dsb[2];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float pv = dev::fast_exp2(s[i] * c2);
-            pb[i >> 3][i & 7] = static_cast<__bf16>(pv);
-            dsb[i >> 3][i & 7] = static_cast<__bf16>(pv * dp[i]);
-        }
-        // dV^T += dO^T P, dK^T += Q^T dS
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(to, base + kStageTile, t, kk), pb[kk], dv[t], 0, 0, 0);
-                dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(to, base, t, kk), dsb[kk], dk[t], 0, 0, 0);
-            }
-
-        // The other stage was last read before the previous barrier.
-        if (more) store_item(st ^ 1);
-        __syncthreads();
+        vmcnt0_barrier();  // the next stage has landed; this one is free
         st ^= 1;
         e = e1;
         r0 = r01;

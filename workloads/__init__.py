@@ -16,7 +16,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-TENSORS = ("q", "k", "v", "do")
+TENSORS = ("q", "k", "v", "do", "lse", "delta")
 
 
 @dataclass(frozen=True)
@@ -86,7 +86,7 @@ def _numpy_sequence(w):
     to fp32."""
     rng = np.random.default_rng(w.seed)
     out = {}
-    for t in TENSORS:
+    for t in ("q", "k", "v", "do"):
         x = rng.standard_normal((w.seq_len, _heads(w, t), w.head_dim))
         out[t] = (x * _std(w, t)).astype(np.float32)
     return out
@@ -120,6 +120,28 @@ def gather(w, tensor, parts, device="cpu"):
     """Concatenate partitions ``parts`` (slot order) into [len*part_len, heads, d]."""
     import torch
     return torch.cat([partition(w, tensor, p, device) for p in parts], dim=0).contiguous()
+
+
+def row_terms(w, parts, device="cpu"):
+    """Synthetic per-row lse and D for the backward, float32 [len*part_len, H_q]:
+    lse uniform in [10, 14) (the size of ln(sum exp) over tens of thousands of
+    keys with unit-variance scores) and D standard normal.  Used where the
+    backward is checked as a function of given lse and D."""
+    import torch
+    out = []
+    for name in ("lse", "delta"):
+        parts_out = []
+        for part in parts:
+            gen = torch.Generator(device=device)
+            gen.manual_seed(stream_seed(w.seed, name, part))
+            shape = (w.part_len, w.heads_q)
+            if name == "lse":
+                x = 10.0 + 4.0 * torch.rand(shape, generator=gen, device=device, dtype=torch.float32)
+            else:
+                x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+            parts_out.append(x)
+        out.append(torch.cat(parts_out, dim=0).contiguous())
+    return out[0], out[1]
 
 
 def torch_dtype(name):

@@ -186,10 +186,12 @@ hipError_t launch_typed(int n, int64_t rows, int chunks_per_row, const u32x4* o_
                         const float* lse_parts, u32x4* o_out, float* lse_out, hipStream_t stream) {
     const int64_t total = rows * chunks_per_row;
     const bool pairs = chunks_per_row % 2 == 0 && n <= 16;
-    // Enough workgroups to fill the chip several times over; each thread then
-    // loops with a grid stride.
+    // One work item per thread (a grid stride only past 2^20 workgroups): a
+    // fully populated grid keeps more loads in flight than a smaller grid
+    // that loops (measured on the 8 x 4Mi-row merge: 5.7 TB/s against 5.2
+    // with 16384 workgroups).
     const int64_t want = ((pairs ? total / 2 : total) + NT - 1) / NT;
-    const unsigned grid = static_cast<unsigned>(want < 256 * 64 ? want : 256 * 64);
+    const unsigned grid = static_cast<unsigned>(want < (1 << 20) ? want : (1 << 20));
 #define MESH_ATTN_MERGE(NMAX)                                                                      \
     hipLaunchKernelGGL((lse_merge_kernel<BF16, NMAX>), dim3(grid), dim3(NT), 0, stream, n, rows,   \
                        chunks_per_row, o_parts, lse_parts, o_out, lse_out)

@@ -67,7 +67,8 @@ hipError_t launch_bwd_delta(int64_t rows, int head_dim, int dtype, const void* o
     const int threads = 256;
     const int64_t rows_per_block = threads >> g_log2;
     const int64_t want = (rows + rows_per_block - 1) / rows_per_block;
-    const unsigned grid = static_cast<unsigned>(want < 16384 ? want : 16384);
+    // one row group per thread group: a fully populated grid keeps the most loads in flight
+    const unsigned grid = static_cast<unsigned>(want < (1 << 20) ? want : (1 << 20));
     const auto* op = static_cast<const u32x4*>(o);
     const auto* dp = static_cast<const u32x4*>(dout);
     if (bf16)

@@ -180,3 +180,48 @@ def test_bwd_delta_matches_oracle(dtype, d, rows):
     err = float(np.max(np.abs(got - ref)))
     say(f"[parity] bwd_delta {dtype} d={d} rows={rows}: max|err|={err:.3e}")
     assert err <= tol
+
+
+def test_tile_bwd_deterministic_and_in_bounds():
+    """Two backward runs are bitwise identical (no atomics, fixed reduction
+    order); guard bands around dq, dk, dv and delta stay untouched."""
+    import torch
+    import long_context_distributed_amd as mat
+    w = _wl((130, (4, 4), (2, 2), True, True, 8, 2))
+    t = _run_case(w)
+    pad = 4096
+
+    def guarded(shape, fill):
+        n = int(np.prod(shape))
+        big = torch.full((n + 2 * pad,), fill, dtype=torch.float32, device="cuda")
+        return big, big[pad:pad + n].view(shape)
+
+    bq, dq2 = guarded(t["dq"].shape, -7.0)
+    bk, dk2 = guarded(t["dk"].shape, 3.5)
+    bv, dv2 = guarded(t["dv"].shape, 9.25)
+    lse, delta = _library_row_terms(w, t["q_parts"], t["do"])
+    bd, delta2 = guarded(delta.shape, 1.5)
+    mat.bwd_delta(_library_row_terms_o(w, t["q_parts"]), t["do"], out=delta2)
+    mat.tile_bwd(t["q"], t["k"], t["v"], t["do"], lse, delta2, t["blocks"], w.part_len,
+                 dq=dq2, dk=dk2, dv=dv2)
+    torch.cuda.synchronize()
+    assert torch.equal(delta2, delta), "row terms not deterministic"
+    for name, a, b in (("dq", dq2, t["dq"]), ("dk", dk2, t["dk"]), ("dv", dv2, t["dv"])):
+        assert torch.equal(a, b), f"{name} not deterministic"
+    for big, fill, name in ((bq, -7.0, "dq"), (bk, 3.5, "dk"), (bv, 9.25, "dv"), (bd, 1.5, "delta")):
+        assert torch.all(big[:pad] == fill) and torch.all(big[-pad:] == fill), f"{name} canary hit"
+
+
+def _library_row_terms_o(w, q_parts):
+    """The rows' final O by the library (as in _library_row_terms)."""
+    import torch
+    import long_context_distributed_amd as mat
+    outs = []
+    for qp in q_parts:
+        blocks = mat.block_list(w.n_parts, 1, qp, 0, w.causal, True)
+        _, kv_parts = tile_geometry(w, blocks)
+        o, _ = mat.tile_fwd(workloads.gather(w, "q", [qp], "cuda"), workloads.gather(w, "k", kv_parts, "cuda"),
+                            workloads.gather(w, "v", kv_parts, "cuda"), blocks, w.part_len,
+                            1.0 / math.sqrt(w.head_dim))
+        outs.append(o)
+    return torch.cat(outs).contiguous()

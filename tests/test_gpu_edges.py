@@ -103,3 +103,28 @@ def test_max_slots_backward(R, C, r, c):
         fro = float(np.linalg.norm(g - ref)) / max(float(np.linalg.norm(ref)), 1e-30)
         say(f"[edge] {R}x{C} backward {name}: max|err|={err:.3e} (max|ref| {top:.3e}) fro={fro:.2e}")
         assert err <= 2e-2 * top + 1e-6 and fro <= 1e-2, name
+
+
+def test_empty_block_list():
+    """No listed block (every pair SKIP): the forward writes (0, -inf) for every
+    row and the backward writes zero gradients, over buffers pre-filled with
+    garbage."""
+    import torch
+    import long_context_distributed_amd as mat
+    w = workloads.small("bf16", 70, 2, 2, 0, 0, True, True, 4, 2, 128)
+    q = workloads.gather(w, "q", [0, 1], "cuda")
+    k = workloads.gather(w, "k", [0, 2], "cuda")
+    v = workloads.gather(w, "v", [0, 2], "cuda")
+    do = workloads.gather(w, "do", [0, 1], "cuda")
+    o = torch.full_like(q, 3.0)
+    lse = torch.full((q.shape[0], 4), 5.0, device="cuda")
+    mat.tile_fwd(q, k, v, [], w.part_len, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    lse_r, delta = workloads.row_terms(w, [0, 1], "cuda")
+    dq = torch.full(q.shape, 7.0, device="cuda")
+    dk = torch.full(k.shape, 7.0, device="cuda")
+    dv = torch.full(v.shape, 7.0, device="cuda")
+    mat.tile_bwd(q, k, v, do, lse_r, delta, [], w.part_len, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)

@@ -139,7 +139,7 @@ def cpu_baseline(w, q, k, v, q_parts, kv_parts, budget_s=12.0):
                       f"softmax over their visible keys, {t_used:.1f} s"}
 
 
-def backward_leg(steps, w, q, k, v, o, lse, q_parts, blocks, fwd_flops, dev):
+def backward_leg(steps, wid, w, q, k, v, o, lse, q_parts, blocks, fwd_flops, dev):
     """Times the tile backward: D = rowsum(dO * O), then dQ and dK/dV."""
     import torch
     import long_context_distributed_amd as mat
@@ -182,18 +182,10 @@ def backward_leg(steps, w, q, k, v, o, lse, q_parts, blocks, fwd_flops, dev):
             "flops": bwd_flops, "executed_flops": exec_flops,
             "executed_tflops": exec_flops / (t_bwd * 1e-3) / 1e12, "steps": steps,
             "kernels": ["tile_bwd_dq_bf16_d128", "tile_bwd_dkdv_bf16_d128"],
-            "traffic": {kn: measured_traffic(kn, w_id(w)) for kn in
+            "traffic": {kn: measured_traffic(kn, wid) for kn in
                         ("tile_bwd_dq_bf16_d128", "tile_bwd_dkdv_bf16_d128")},
             "row_terms": {"ms": t_delta, "bytes": dbytes,
                           "gbs": dbytes / (t_delta * 1e-3) / 1e9}}
-
-
-def w_id(w):
-    import workloads
-    for i, x in workloads.WORKLOADS.items():
-        if x is w:
-            return i
-    return None
 
 
 def main():
@@ -336,8 +328,8 @@ def main():
                      "kernel": tile_kernel},
     }
     if a.backward_steps > 0 and w.dtype == "bf16":
-        result["tile_bwd"] = backward_leg(a.backward_steps, w, q, k, v, o_own, l_own, q_parts,
-                                          blocks, flops, dev)
+        result["tile_bwd"] = backward_leg(a.backward_steps, a.workload, w, q, k, v, o_own, l_own,
+                                          q_parts, blocks, flops, dev)
     if a.copy_calibration > 0:
         src = torch.empty(a.copy_calibration << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -47,6 +47,25 @@ def main():
                    "q": q.tolist(), "k": k.tolist(), "v": v.tolist(),
                    "o": o.tolist(), "lse": lse.tolist()}, f)
 
+    # The backward of the same tile: dO quantised the same way; the rows' final
+    # lse and D over the whole sequence (all four partitions), then the tile's
+    # gradient shares.
+    do = np.round(r.standard_normal((6, 2, 4)) * 8) / 8
+    kall = np.round(r.standard_normal((12, 1, 4)) * 8) / 8
+    vall = np.round(r.standard_normal((12, 1, 4)) * 8) / 8
+    kall[[p * 3 + i for p in kvset for i in range(3)]] = k
+    vall[[p * 3 + i for p in kvset for i in range(3)]] = v
+    qpos = oracle.tile_positions_ref(qset, 3)
+    o_f, lse_f = oracle.attention_ref(q, kall, vall, qpos, np.arange(12), True, 0.5)
+    delta = oracle.bwd_delta_ref(o_f, do)
+    dq, dk, dv = oracle.tile_bwd_ref(q, k, v, do, lse_f, delta, qset, kvset, 3, True, 0.5)
+    with open(os.path.join(HERE, "tiny_tile_bwd.json"), "w") as f:
+        json.dump({"mesh": [2, 2], "tile": [1, 0], "part_len": 3, "causal": True, "scale": 0.5,
+                   "q_parts": qset, "kv_parts": kvset, "q": q.tolist(), "k_all": kall.tolist(),
+                   "v_all": vall.tolist(), "do": do.tolist(), "lse": lse_f.tolist(),
+                   "delta": delta.tolist(), "dq": dq.tolist(), "dk": dk.tolist(),
+                   "dv": dv.tolist()}, f)
+
 
 if __name__ == "__main__":
     main()

@@ -182,22 +182,23 @@ using namespace mesh_attn;
 
 extern "C" int mesh_attn_tile_fwd(const mesh_attn_tile_desc* desc, const void* q, const void* k,
                                   const void* v, void* o, float* lse, void* hip_stream) {
-    if (desc == nullptr) return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: desc is NULL");
+    const char* who = "tile_fwd";
+    if (desc == nullptr) return failw(MESH_ATTN_ERR_INVALID, who, "desc is NULL");
     const mesh_attn_tile_desc& d = *desc;
     if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr)
-        return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: NULL tensor pointer");
+        return failw(MESH_ATTN_ERR_INVALID, who, "NULL tensor pointer");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-        return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: tensor pointer not 16-byte aligned");
-    const int shape_st = check_tile_shape("tile_fwd", d);
+        return failw(MESH_ATTN_ERR_INVALID, who, "tensor pointer not 16-byte aligned");
+    const int shape_st = check_tile_shape(who, d);
     if (shape_st != MESH_ATTN_OK) return shape_st;
     const bool supported = (d.dtype == MESH_ATTN_BF16 && d.head_dim == 128) ||
                            (d.dtype == MESH_ATTN_F32 && (d.head_dim == 64 || d.head_dim == 128));
     if (!supported)
-        return fail(MESH_ATTN_ERR_UNSUPPORTED, "tile_fwd: dtype/head_dim combination not built");
+        return failw(MESH_ATTN_ERR_UNSUPPORTED, who, "dtype/head_dim combination not built");
 
     TileParams p;
     memset(&p, 0, sizeof(p));
-    const int st = build_schedule("tile_fwd", d, p.sched, nullptr);
+    const int st = build_schedule(who, d, p.sched, nullptr);
     if (st != MESH_ATTN_OK) return st;
 
     p.q = q;
@@ -211,7 +212,7 @@ extern "C" int mesh_attn_tile_fwd(const mesh_attn_tile_desc* desc, const void* q
 
     const int64_t n_wg = static_cast<int64_t>(d.n_q_slots) * p.n_tok_blocks * d.heads_kv *
                          p.n_head_groups;
-    if (n_wg > INT32_MAX) return fail(MESH_ATTN_ERR_INVALID, "tile_fwd: grid too large");
+    if (n_wg > INT32_MAX) return failw(MESH_ATTN_ERR_INVALID, who, "grid too large");
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     const hipError_t e = d.dtype == MESH_ATTN_BF16 ? launch_tile_fwd_bf16(p, d.head_dim, stream)
@@ -222,23 +223,24 @@ extern "C" int mesh_attn_tile_fwd(const mesh_attn_tile_desc* desc, const void* q
 extern "C" int mesh_attn_lse_merge(int32_t n_parts, int64_t rows, int32_t head_dim, int32_t dtype,
                                    const void* o_parts, const float* lse_parts, void* o_out,
                                    float* lse_out, void* hip_stream) {
+    const char* who = "lse_merge";
     if (n_parts < 1 || n_parts > 64)
-        return fail(MESH_ATTN_ERR_INVALID, "lse_merge: n_parts must be in 1..64");
-    if (rows < 0) return fail(MESH_ATTN_ERR_INVALID, "lse_merge: rows must be >= 0");
+        return failw(MESH_ATTN_ERR_INVALID, who, "n_parts must be in 1..64");
+    if (rows < 0) return failw(MESH_ATTN_ERR_INVALID, who, "rows must be >= 0");
     if (dtype != MESH_ATTN_BF16 && dtype != MESH_ATTN_F32)
-        return fail(MESH_ATTN_ERR_INVALID, "lse_merge: unknown dtype");
+        return failw(MESH_ATTN_ERR_INVALID, who, "unknown dtype");
     const int vec = dtype == MESH_ATTN_BF16 ? 8 : 4;
     if (head_dim < 8 || head_dim > 512 || head_dim % vec != 0)
-        return fail(MESH_ATTN_ERR_INVALID, "lse_merge: head_dim must be a multiple of 8 (bf16) "
+        return failw(MESH_ATTN_ERR_INVALID, who, "head_dim must be a multiple of 8 (bf16) "
                                            "or 4 (f32) in 8..512");
     if (o_parts == nullptr || lse_parts == nullptr || o_out == nullptr)
-        return fail(MESH_ATTN_ERR_INVALID, "lse_merge: NULL tensor pointer");
+        return failw(MESH_ATTN_ERR_INVALID, who, "NULL tensor pointer");
     if (!aligned16(o_parts) || !aligned16(o_out) ||
         (reinterpret_cast<uintptr_t>(lse_parts) & 3u) != 0 ||
         (lse_out != nullptr && (reinterpret_cast<uintptr_t>(lse_out) & 3u) != 0))
-        return fail(MESH_ATTN_ERR_INVALID, "lse_merge: misaligned pointer");
+        return failw(MESH_ATTN_ERR_INVALID, who, "misaligned pointer");
     if (rows > (INT64_MAX / 64) / head_dim)
-        return fail(MESH_ATTN_ERR_INVALID, "lse_merge: rows too large");
+        return failw(MESH_ATTN_ERR_INVALID, who, "rows too large");
     if (rows == 0) {
         clear_error();
         return MESH_ATTN_OK;

@@ -101,26 +101,12 @@ def merge_bytes(n, rows, d, elt):
     return n * rows * (d * elt + 4) + rows * (d * elt + 4)
 
 
-def cpu_baseline(w, q, k, v, q_parts, kv_parts, budget_s=12.0):
-    """The oracle, as it stands, on a bounded sample of query rows of the tile."""
+def _oracle_rows_rate(w, qh, kh, vh, qpos, kpos, rows_all, budget_s):
+    """Times oracle.attention_ref on batches of sampled rows for about
+    budget_s seconds; returns (flops per second, rows done, seconds used)."""
     import numpy as np
     import oracle
-    import workloads
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
     scale = 1.0 / math.sqrt(w.head_dim)
-    qh = q.detach().cpu().double().numpy()
-    kh = k.detach().cpu().double().numpy()
-    vh = v.detach().cpu().double().numpy()
-    qpos = oracle.tile_positions_ref(q_parts, w.part_len)
-    kpos = oracle.tile_positions_ref(kv_parts, w.part_len)
-    rows_all = workloads.sample_rows(q.shape[0], w.heads_q, w.heads_kv, w.part_len,
-                                     n_sample=200000, seed=3)
-    rng = np.random.default_rng(7)
-    rows_all = rows_all[rng.permutation(len(rows_all))]
     done, flops, t_used, batch = 0, 0.0, 0.0, 16
     while t_used < budget_s and done < len(rows_all):
         rows = rows_all[done:done + batch]
@@ -133,10 +119,55 @@ def cpu_baseline(w, q, k, v, q_parts, kv_parts, budget_s=12.0):
         t_used += dt
         done += len(rows)
         batch = min(4 * batch, max(16, int(len(rows) * (budget_s - t_used) / max(dt, 1e-3))))
-    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+    return flops / max(t_used, 1e-9), done, t_used
+
+
+def cpu_baseline(w, q, k, v, q_parts, kv_parts, tile_flops_total, o_parts, l_parts, budget_s=12.0):
+    """The oracle, as it stands, on bounded samples of the same workload:
+    sampled query rows of the tile on every host core (the reported value),
+    the same on one core, and the merge oracle on sampled rows of the merge's
+    partials."""
+    import numpy as np
+    import oracle
+    import workloads
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    qh = q.detach().cpu().double().numpy()
+    kh = k.detach().cpu().double().numpy()
+    vh = v.detach().cpu().double().numpy()
+    qpos = oracle.tile_positions_ref(q_parts, w.part_len)
+    kpos = oracle.tile_positions_ref(kv_parts, w.part_len)
+    rows_all = workloads.sample_rows(q.shape[0], w.heads_q, w.heads_kv, w.part_len,
+                                     n_sample=200000, seed=3)
+    rows_all = rows_all[np.random.default_rng(7).permutation(len(rows_all))]
+    rate, done, t_used = _oracle_rows_rate(w, qh, kh, vh, qpos, kpos, rows_all, 0.6 * budget_s)
+    rest = rows_all[done:] if done < len(rows_all) else rows_all  # a small tile is timed again
+    with threadpool_limits(limits=1):
+        rate1, done1, t1 = _oracle_rows_rate(w, qh, kh, vh, qpos, kpos, rest, 0.25 * budget_s)
+    # Merge oracle: contiguous blocks of rows of the partials, all n parts.
+    n_parts, rows, d = o_parts.shape
+    gen = np.random.default_rng(8)
+    m_rows, m_bytes, m_t = 0, 0.0, 0.0
+    while m_t < 0.15 * budget_s and m_rows < rows:
+        r0 = int(gen.integers(0, max(rows - 4096, 1)))
+        op = o_parts[:, r0:r0 + 4096].float().cpu().numpy()
+        lp = l_parts[:, r0:r0 + 4096].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.lse_merge_ref(op, lp)
+        m_t += time.perf_counter() - t0
+        m_rows += op.shape[1]
+        m_bytes += merge_bytes(n_parts, op.shape[1], d, o_parts.element_size())
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{done} (token, head) rows of the same tile, exact float64 two-pass "
-                      f"softmax over their visible keys, {t_used:.1f} s"}
+                      f"softmax over their visible keys, {t_used:.1f} s",
+            "full_tile_s_extrapolated": tile_flops_total / rate,
+            "single_core": {"value": rate1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                            "sample": f"{done1} rows of the same tile on one core, {t1:.1f} s"},
+            "merge": {"value": m_bytes / max(m_t, 1e-9) / 1e9, "unit": "GB/s",
+                      "cores": int(threads),
+                      "sample": f"{m_rows} merged rows of the {n_parts} partials, float64, "
+                                f"{m_t:.1f} s"}}
 
 
 def backward_leg(steps, wid, w, q, k, v, o, lse, q_parts, blocks, fwd_flops, dev):
@@ -338,7 +369,8 @@ def main():
         log(f"[bench] copy calibration: {a.copy_calibration} MiB read + written by one copy kernel")
     if not a.no_cpu_baseline:
         log("[bench] timing the oracle on host cores")
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, q_parts, kv_parts, a.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, q_parts, kv_parts, flops, o_parts,
+                                              l_parts, a.cpu_budget)
     print(json.dumps(result), flush=True)
 
 

@@ -1,0 +1,56 @@
+"""Host-side pieces of bench.py: the algorithmic work counts and the oracle
+baseline leg, run on CPU tensors of a small workload."""
+import math
+import os
+import sys
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import oracle  # noqa: E402
+import workloads  # noqa: E402
+
+
+def test_tile_flops_counts_visible_pairs():
+    """4*d flops per visible pair and query head: a causal 4x4 rotated tile
+    (2,2) has 9 FULL blocks, 1 DIAG block and 6 SKIP blocks."""
+    blocks = oracle.block_list_ref(4, 4, 2, 2, True, True)
+    L, hq, d = 8, 3, 16
+    want = 4 * d * hq * (9 * L * L + L * (L + 1) // 2)
+    assert bench.tile_flops(blocks, L, hq, d) == want
+    # brute force over token positions gives the same pair count
+    q_parts = [b[2] for b in blocks if b[1] == 0]
+    kv_parts = [b[3] for b in blocks if b[0] == 0]
+    qp = oracle.tile_positions_ref(q_parts, L)
+    kp = oracle.tile_positions_ref(kv_parts, L)
+    assert 4 * d * hq * int((kp[None, :] <= qp[:, None]).sum()) == want
+
+
+def test_merge_bytes():
+    # n partial rows of d bf16 values and one fp32 lse each, plus the output row
+    assert bench.merge_bytes(8, 10, 128, 2) == 8 * 10 * 260 + 10 * 260
+
+
+def test_cpu_baseline_leg_reports_all_runs():
+    w = workloads.WORKLOADS[1]
+    blocks = oracle.block_list_ref(w.mesh_rows, w.mesh_cols, w.tile_row, w.tile_col,
+                                   w.causal, w.kv_rotate)
+    q_parts = [b[2] for b in blocks if b[1] == 0]
+    kv_parts = [b[3] for b in blocks if b[0] == 0]
+    q = workloads.gather(w, "q", q_parts, "cpu")
+    k = workloads.gather(w, "k", kv_parts, "cpu")
+    v = workloads.gather(w, "v", kv_parts, "cpu")
+    rows = q.shape[0] * w.heads_q
+    o_parts = torch.randn((2, rows, w.head_dim))
+    l_parts = torch.randn((2, rows))
+    flops = bench.tile_flops(blocks, w.part_len, w.heads_q, w.head_dim)
+    res = bench.cpu_baseline(w, q, k, v, q_parts, kv_parts, flops, o_parts, l_parts, budget_s=0.5)
+    assert res["kind"] == "oracle" and res["unit"] == "TFLOP/s" and res["cores"] >= 1
+    assert res["value"] > 0 and res["single_core"]["value"] > 0 and res["single_core"]["cores"] == 1
+    assert math.isclose(res["full_tile_s_extrapolated"], flops / (res["value"] * 1e12), rel_tol=1e-9)
+    assert res["merge"]["unit"] == "GB/s" and res["merge"]["value"] > 0
+    assert np.isfinite(res["merge"]["value"])

@@ -116,6 +116,80 @@ def test_host_code_under_asan_and_ubsan(tmp_path):
     assert "runtime error" not in res.stderr and "AddressSanitizer" not in res.stderr
 
 
+THREADS_DRIVER = r"""
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+#include "mesh_attn.h"
+
+static std::atomic<int> bad{0};
+
+static void worker(int t) {
+    mesh_attn_block blocks[MESH_ATTN_MAX_BLOCKS];
+    int32_t n = 0;
+    const int R = 4 + 2 * (t % 4), C = 4;
+    void* fake = reinterpret_cast<void*>(0x100000);
+    for (int it = 0; it < 2000; ++it) {
+        // a valid block list, a valid tile (reaches the stub launch), an invalid tile
+        if (mesh_attn_block_list(R, C, R / 2, C / 2, 1, 1, blocks, MESH_ATTN_MAX_BLOCKS, &n) !=
+                MESH_ATTN_OK || n != R * C)
+            ++bad;
+        if (mesh_attn_last_error()[0] != 0) ++bad;
+        mesh_attn_tile_desc d = {MESH_ATTN_BF16, 64, C, R, 4, 2, 128, 0.1f, blocks, n};
+        if (mesh_attn_tile_fwd(&d, fake, fake, fake, fake, static_cast<float*>(fake), nullptr) !=
+            MESH_ATTN_ERR_HIP)
+            ++bad;
+        if (mesh_attn_tile_bwd(&d, fake, fake, fake, fake, static_cast<float*>(fake),
+                               static_cast<float*>(fake), static_cast<float*>(fake),
+                               static_cast<float*>(fake), static_cast<float*>(fake), nullptr) !=
+            MESH_ATTN_ERR_HIP)
+            ++bad;
+        d.part_len = 0;
+        if (mesh_attn_tile_fwd(&d, fake, fake, fake, fake, static_cast<float*>(fake), nullptr) !=
+            MESH_ATTN_ERR_INVALID)
+            ++bad;
+        if (std::strcmp(mesh_attn_last_error(), "tile_fwd: part_len must be >= 1") != 0) ++bad;
+    }
+}
+
+int main() {
+    std::vector<std::thread> th;
+    for (int t = 0; t < 8; ++t) th.emplace_back(worker, t);
+    for (auto& x : th) x.join();
+    std::printf("threads ok, bad=%d\n", bad.load());
+    return bad.load() == 0 ? 0 : 1;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("g++") is None or not os.path.exists("/opt/rocm/include/hip"),
+                    reason="needs g++ and the HIP headers")
+def test_host_code_under_tsan(tmp_path):
+    """Eight native threads call the C ABI at once (valid and invalid tiles,
+    block lists) with the host code built under ThreadSanitizer; each thread
+    must see its own results and last-error text, and TSan must find no race."""
+    if not _runtime("libtsan.so"):
+        pytest.skip("ThreadSanitizer runtime not installed")
+    (tmp_path / "stub.cpp").write_text(STUB)
+    (tmp_path / "driver.cpp").write_text(THREADS_DRIVER)
+    exe = tmp_path / "threads"
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=thread", "-D__HIP_PLATFORM_AMD__",
+           "-I/opt/rocm/include", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "block_list.cpp"),
+           str(tmp_path / "stub.cpp"), str(tmp_path / "driver.cpp"), "-o", str(exe),
+           "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-pthread"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1:exitcode=66")
+    res = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=300)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "threads ok, bad=0" in res.stdout
+    assert "ThreadSanitizer" not in res.stderr
+
+
 def test_bench_refuses_more_than_one_gpu():
     res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                          capture_output=True, text=True, timeout=120)

@@ -237,3 +237,47 @@ def test_bwd_delta_invalid(lib, kw):
 
 def test_bwd_delta_zero_rows_is_a_noop(lib):
     assert lib.mesh_attn_bwd_delta(0, 128, _lib.BF16, FAKE, FAKE, FAKE, None) == _lib.OK
+
+
+# ----------------------------------------------------------------------------- threads
+
+THREAD_CASES = [
+    (dict(dtype=7), b"tile_fwd: unknown dtype"),
+    (dict(part_len=0), b"tile_fwd: part_len must be >= 1"),
+    (dict(heads_q=3, heads_kv=2), b"tile_fwd: heads_q must be a positive multiple of heads_kv"),
+    (dict(softmax_scale=-1.0), b"tile_fwd: softmax_scale must be finite and > 0"),
+]
+
+
+def test_calls_are_thread_safe(lib):
+    """Threads calling at once (ctypes drops the GIL around each call): every
+    thread reads back its own last error, a successful block_list clears it,
+    and the block lists computed concurrently equal the oracle's."""
+    import threading
+    meshes = [(4, 4, 2, 2), (8, 8, 4, 4), (16, 4, 8, 2), (3, 5, 1, 4)]
+    want = {m: oracle.block_list_ref(*m, True, True) for m in meshes}
+    failures = []
+    start = threading.Barrier(8)
+
+    def work(t):
+        kw, msg = THREAD_CASES[t % len(THREAD_CASES)]
+        m = meshes[t % len(meshes)]
+        desc = _desc(**kw)
+        start.wait()
+        for it in range(300):
+            if _tile(lib, desc) != _lib.ERR_INVALID:
+                failures.append((t, it, "status"))
+            err = lib.mesh_attn_last_error()
+            if err != msg:
+                failures.append((t, it, err))
+            if _lib_block_list(lib, *m, 1, 1) != want[m]:
+                failures.append((t, it, "block list"))
+            if lib.mesh_attn_last_error() != b"":
+                failures.append((t, it, "not cleared"))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not failures, failures[:5]

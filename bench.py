@@ -56,12 +56,28 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_sha256(kernel):
+def code_only(text):
+    """C/C++ source without comments and with whitespace runs collapsed, so
+    that a key built from it changes when the code changes and not when only
+    a comment does.  (The sources hold no comment markers inside strings.)"""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def source_sha256(kernel, read=None):
+    """Key of the code a kernel is built from: sha256 over its source files'
+    code (comments and whitespace runs ignored).  read(name) -> text defaults
+    to the files in csrc/."""
     import hashlib
+    if read is None:
+        def read(name):
+            with open(os.path.join(ROOT, "long_context_distributed_amd", "csrc", name)) as f:
+                return f.read()
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "long_context_distributed_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        h.update(code_only(read(name)).encode())
     return h.hexdigest()
 
 

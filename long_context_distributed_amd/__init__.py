@@ -63,20 +63,44 @@ def _dtype_code(t):
 
 def _stream_handle(stream, device):
     import torch
+    if stream is not None and stream.device != device:
+        raise ValueError(f"stream is on {stream.device}, the tensors on {device}")
     s = stream if stream is not None else torch.cuda.current_stream(device)
     return ctypes.c_void_p(s.cuda_stream)
 
 
 def _require_device(*ts):
+    """Every tensor contiguous and on one HIP device (there is no CPU path)."""
+    dev = None
     for t in ts:
         if not t.is_cuda:
             raise ValueError("tensors must be on a HIP device (no CPU path)")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors must be on one device ({dev} and {t.device})")
+
+
+def _no_overlap(outs, ins):
+    """Outputs may overlap neither the inputs nor each other (the kernels
+    read inputs while writing outputs)."""
+    def span(t):
+        a = t.data_ptr()
+        return a, a + t.numel() * t.element_size()
+    for i, o in enumerate(outs):
+        a0, a1 = span(o)
+        for x in list(ins) + list(outs[i + 1:]):
+            b0, b1 = span(x)
+            if a0 < b1 and b0 < a1:
+                raise ValueError("output buffers must not overlap the inputs or each other")
 
 
 def _tile_desc(q, k, v, blocks, part_len, softmax_scale):
     _require_device(q, k, v)
+    if int(part_len) < 1:
+        raise ValueError("part_len must be >= 1")
     if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
         raise ValueError("expected q [Tq, Hq, d] and k, v [Tk, Hkv, d]")
     if q.dtype != k.dtype or q.dtype != v.dtype:
@@ -114,10 +138,11 @@ def tile_fwd(q, k, v, blocks, part_len, softmax_scale=None, out=None, lse=None, 
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
-    _require_device(out, lse)
+    _require_device(q, k, v, out, lse)
     if out.shape != q.shape or out.dtype != q.dtype or lse.shape != (tq, hq) or \
             lse.dtype != torch.float32:
         raise ValueError("output buffers have the wrong shape or dtype")
+    _no_overlap([out, lse], [q, k, v])
     _check(lib, lib.mesh_attn_tile_fwd(ctypes.byref(desc), q.data_ptr(), k.data_ptr(),
                                        v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                        _stream_handle(stream, q.device)))
@@ -139,9 +164,13 @@ def lse_merge(o_parts, lse_parts, out=None, lse_out=None, want_lse=True, stream=
         out = torch.empty((rows, d), dtype=o_parts.dtype, device=o_parts.device)
     if want_lse and lse_out is None:
         lse_out = torch.empty((rows,), dtype=torch.float32, device=o_parts.device)
-    _require_device(out)
+    outs = [out] + ([lse_out] if lse_out is not None else [])
+    _require_device(o_parts, lse_parts, *outs)
     if out.shape != (rows, d) or out.dtype != o_parts.dtype:
         raise ValueError("output buffer has the wrong shape or dtype")
+    if lse_out is not None and (lse_out.shape != (rows,) or lse_out.dtype != torch.float32):
+        raise ValueError("lse_out must be float32 [rows]")
+    _no_overlap(outs, [o_parts, lse_parts])
     _check(lib, lib.mesh_attn_lse_merge(n, rows, d, _dtype_code(o_parts), o_parts.data_ptr(),
                                         lse_parts.data_ptr(), out.data_ptr(),
                                         lse_out.data_ptr() if lse_out is not None else None,
@@ -161,9 +190,10 @@ def bwd_delta(o, dout, out=None, stream=None):
     rows = o.numel() // d if d else 0
     if out is None:
         out = torch.empty(o.shape[:-1], dtype=torch.float32, device=o.device)
-    _require_device(out)
+    _require_device(o, dout, out)
     if out.shape != o.shape[:-1] or out.dtype != torch.float32:
         raise ValueError("output buffer has the wrong shape or dtype")
+    _no_overlap([out], [o, dout])
     _check(lib, lib.mesh_attn_bwd_delta(rows, d, _dtype_code(o), o.data_ptr(), dout.data_ptr(),
                                         out.data_ptr(), _stream_handle(stream, o.device)))
     return out
@@ -194,10 +224,11 @@ def tile_bwd(q, k, v, dout, lse, delta, blocks, part_len, softmax_scale=None, dq
         dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
     if dv is None:
         dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
-    _require_device(dq, dk, dv)
+    _require_device(q, k, v, dout, lse, delta, dq, dk, dv)
     if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape or \
             any(t.dtype != torch.float32 for t in (dq, dk, dv)):
         raise ValueError("gradient buffers have the wrong shape or dtype")
+    _no_overlap([dq, dk, dv], [q, k, v, dout, lse, delta])
     _check(lib, lib.mesh_attn_tile_bwd(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                        dout.data_ptr(), lse.data_ptr(), delta.data_ptr(),
                                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),

@@ -273,13 +273,14 @@ __global__ __launch_bounds__(NT, 1) void tile_fwd_bf16_d128(const TileParams p) 
     const int b_end = p.sched.blk_off[w.q_slot + 1];
 
     // The tiles of this Q slot form one sequence over (block, key tile); tile
-    // t lives in LDS buffer t % 3.  The work runs over 32-key halves j with a
+    // t lives in LDS buffer t % 5.  The work runs over 32-key halves j with a
     // software pipeline: the QK^T MFMAs of half j+1 are issued together with
     // the exponentials of half j, and the PV MFMAs of half j together with the
-    // row maximum of half j+1.  Stepping into tile t+1, the waves wait for its
-    // DMA and meet at a barrier; tile t's V is still read after it (the PV of
-    // its last half), so the DMA started there, for tile t+2, goes into tile
-    // t-1's buffer, which every wave finished before the barrier.
+    // row maximum of half j+1.  Stepping from an odd tile t into tile t+1, the
+    // waves wait for their DMA of tiles t+1 and t+2 and meet at a barrier;
+    // tile t's V is still read after it (the PV of its last half), so the DMA
+    // started there, for tiles t+3 and t+4, goes into the buffers of tiles t-2
+    // and t-1, which every wave finished before the barrier.
     auto tile_end = [&](int bi_) {
         return (sched_entry(p.sched, bi_) & 3) == kDiag ? w.wg_tok_end : L;
     };

@@ -54,3 +54,38 @@ def test_cpu_baseline_leg_reports_all_runs():
     assert math.isclose(res["full_tile_s_extrapolated"], flops / (res["value"] * 1e12), rel_tol=1e-9)
     assert res["merge"]["unit"] == "GB/s" and res["merge"]["value"] > 0
     assert np.isfinite(res["merge"]["value"])
+
+
+def test_source_key_ignores_comments_only():
+    """The key that ties counter summaries to a kernel's code: equal for a
+    comment or whitespace edit, different for a code edit."""
+    base = "int f(int x) {\n    return x + 1;  // one more\n}\n/* block\n comment */\n"
+    assert bench.code_only(base) == bench.code_only(base.replace("one more", "plus one"))
+    assert bench.code_only(base) == bench.code_only(base.replace("    return", "  return"))
+    assert bench.code_only(base) != bench.code_only(base.replace("x + 1", "x + 2"))
+    files = {"a.hip": base, "b.h": "#define N 4\n"}
+    k0 = bench.source_sha256("tile_fwd_bf16_d128", lambda n: files.get(n, base))
+    k1 = bench.source_sha256("tile_fwd_bf16_d128", lambda n: files.get(n, base).replace("// one", "// 1"))
+    k2 = bench.source_sha256("tile_fwd_bf16_d128", lambda n: files.get(n, base).replace("+ 1", "+ 3"))
+    assert k0 == k1 != k2
+
+
+def test_profile_summaries_are_well_formed():
+    """Every counter summary in profiles/ names a kernel bench.py knows, keys
+    the code it measured with a sha256, gives positive traffic, and lists
+    commands that run committed files only (bench.py under rocprofv3)."""
+    import glob
+    import re
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md")))
+    assert paths
+    for path in paths:
+        text = open(path).read()
+        kernel = re.search(r"^- kernel: `([^`]+)`", text, re.M).group(1)
+        assert kernel in bench.KERNEL_SOURCES, path
+        assert re.search(r"^- source_sha256: `[0-9a-f]{64}`", text, re.M), path
+        assert float(re.search(r"^- hbm_bytes_per_launch: `([^`]+)`", text, re.M).group(1)) > 0
+        cmds = [ln.strip() for ln in text.splitlines() if ln.strip().startswith("rocprofv3 ")]
+        assert cmds and all(c.endswith(".py --steps 3 --warmup 1 --no-cpu-baseline "
+                                       "--copy-calibration 1024") and " -- python bench.py" in c
+                            for c in cmds), path
+        assert "_work" not in text, path

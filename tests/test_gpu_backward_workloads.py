@@ -49,7 +49,7 @@ def _f64(t):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("wid", [3, 4, 5])
+@pytest.mark.parametrize("wid", [2, 3, 4, 5])
 def test_backward_workload(wid):
     import torch
     import long_context_distributed_amd as mat

@@ -77,6 +77,8 @@ typedef struct {
 #define MESH_ATTN_MAX_Q_SLOTS 64
 #define MESH_ATTN_MAX_KV_SLOTS 64
 #define MESH_ATTN_MAX_BLOCKS 1024
+/* Most query heads per tile (keeps a token row of every tensor under 2 MiB). */
+#define MESH_ATTN_MAX_HEADS 4096
 
 /*
  * mesh_attn_block_list - the blocks GPU (row, col) of a mesh_rows x mesh_cols
@@ -109,7 +111,7 @@ typedef struct {
     int32_t part_len;       /* L: tokens per partition, >= 1 */
     int32_t n_q_slots;      /* Q partitions in the tile, 1 .. MESH_ATTN_MAX_Q_SLOTS */
     int32_t n_kv_slots;     /* KV partitions in the tile, 1 .. MESH_ATTN_MAX_KV_SLOTS */
-    int32_t heads_q;        /* H_q >= 1 */
+    int32_t heads_q;        /* H_q, 1 .. MESH_ATTN_MAX_HEADS */
     int32_t heads_kv;       /* H_kv >= 1, divides H_q; query head h reads KV head h / (H_q/H_kv) */
     int32_t head_dim;       /* d: 128 for bf16; 64 or 128 for f32 */
     float softmax_scale;    /* finite and > 0; usually 1/sqrt(d) */

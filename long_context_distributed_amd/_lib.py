@@ -25,6 +25,7 @@ SKIP = 2
 MAX_Q_SLOTS = 64
 MAX_KV_SLOTS = 64
 MAX_BLOCKS = 1024
+MAX_HEADS = 4096
 
 # Every symbol include/mesh_attn.h declares.
 EXPORTS = ("mesh_attn_block_list", "mesh_attn_tile_fwd", "mesh_attn_lse_merge",

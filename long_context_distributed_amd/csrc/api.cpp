@@ -146,6 +146,8 @@ static int check_tile_shape(const char* who, const mesh_attn_tile_desc& d) {
         return failw(MESH_ATTN_ERR_INVALID, who, "n_kv_slots out of range");
     if (d.heads_q < 1 || d.heads_kv < 1 || d.heads_q % d.heads_kv != 0)
         return failw(MESH_ATTN_ERR_INVALID, who, "heads_q must be a positive multiple of heads_kv");
+    if (d.heads_q > MESH_ATTN_MAX_HEADS)
+        return failw(MESH_ATTN_ERR_INVALID, who, "heads_q above MESH_ATTN_MAX_HEADS");
     if (d.head_dim < 1) return failw(MESH_ATTN_ERR_INVALID, who, "head_dim must be >= 1");
     if (!(isfinite(d.softmax_scale) && d.softmax_scale > 0.0f))
         return failw(MESH_ATTN_ERR_INVALID, who, "softmax_scale must be finite and > 0");

@@ -71,17 +71,24 @@ static_assert(kBwdRowsPerWave == 32, "one 32-row (32-key) block per wave");
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
-// Buffer resource over `rows` rows of `row_bytes` from base: reads of rows at
-// or past `rows` return zero.
-__device__ __forceinline__ Rsrc rows_rsrc(const void* base, int rows, int row_bytes) {
-    const int n = rows > 0 ? (rows - 1) * row_bytes + kRowBytes : 0;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcWord3);
+// Byte range of a descriptor that serves at most `max_rows` rows of
+// `row_bytes` from its base, of which `rows` exist: reads of rows at or past
+// `rows` return zero.  Clamping to the rows actually read keeps the range in
+// 32 bits however long the partition is.
+__device__ __forceinline__ int rows_range(int rows, int max_rows, int row_bytes) {
+    const int r = rows < max_rows ? rows : max_rows;
+    return r > 0 ? (r - 1) * row_bytes + kRowBytes : 0;
+}
+
+__device__ __forceinline__ Rsrc rows_rsrc(const void* base, int rows, int max_rows, int row_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                             rows_range(rows, max_rows, row_bytes), kRsrcWord3);
 }
 
 // The same as raw descriptor words, for the DMA loads.
-__device__ __forceinline__ u32x4 rows_desc(const void* base, int rows, int row_bytes) {
+__device__ __forceinline__ u32x4 rows_desc(const void* base, int rows, int max_rows, int row_bytes) {
     const unsigned long long a = reinterpret_cast<unsigned long long>(base);
-    const int n = rows > 0 ? (rows - 1) * row_bytes + kRowBytes : 0;
+    const int n = rows_range(rows, max_rows, row_bytes);
     return u32x4{static_cast<unsigned>(a), static_cast<unsigned>(a >> 32) & 0xffffu,
                  static_cast<unsigned>(n), static_cast<unsigned>(kRsrcWord3)};
 }
@@ -183,8 +190,8 @@ __global__ __launch_bounds__(QT, 1) void tile_bwd_dq_bf16_d128(const BwdDqParams
     {
         const int qrow_bytes = p.heads_q * kRowBytes;
         const size_t first = ((size_t)(w.q_slot * L + w.wave_tok0) * p.heads_q + w.head) * D;
-        const Rsrc qr = rows_rsrc(reinterpret_cast<const __bf16*>(p.q) + first, L - w.wave_tok0, qrow_bytes);
-        const Rsrc dr = rows_rsrc(reinterpret_cast<const __bf16*>(p.dout) + first, L - w.wave_tok0,
+        const Rsrc qr = rows_rsrc(reinterpret_cast<const __bf16*>(p.q) + first, L - w.wave_tok0, 32, qrow_bytes);
+        const Rsrc dr = rows_rsrc(reinterpret_cast<const __bf16*>(p.dout) + first, L - w.wave_tok0, 32,
                                   qrow_bytes);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -222,8 +229,8 @@ __global__ __launch_bounds__(QT, 1) void tile_bwd_dq_bf16_d128(const BwdDqParams
     const unsigned lds0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>((LDS_AS unsigned char*)smem));
     auto issue = [&](int bi_, int n0_, int buf_) {
         const size_t off = (size_t)(sched_entry(p.sched, bi_) >> 2) * slot_elems + (size_t)n0_ * p.heads_kv * D;
-        const u32x4 kr = rows_desc(kbase + off, L - n0_, row_bytes);
-        const u32x4 vr = rows_desc(vbase + off, L - n0_, row_bytes);
+        const u32x4 kr = rows_desc(kbase + off, L - n0_, BN, row_bytes);
+        const u32x4 vr = rows_desc(vbase + off, L - n0_, BN, row_bytes);
         const unsigned dst = lds0 + buf_ * kBufBytes;
 #pragma unroll
         for (int i = 0; i < kDmaPerWave; ++i) {
@@ -393,7 +400,7 @@ __global__ __launch_bounds__(KT, 1) void tile_bwd_dkdv_bf16_d128(const BwdDkvPar
     // dP = dO V^T: key r32 of this wave, dims 16c + 8g ..) into registers.
     const size_t kv_first = ((size_t)(kv_slot * L + key0) * p.heads_kv + kv_head) * D;
     {
-        const Rsrc kr = rows_rsrc(reinterpret_cast<const __bf16*>(p.k) + kv_first, L - key0, kv_row_bytes);
+        const Rsrc kr = rows_rsrc(reinterpret_cast<const __bf16*>(p.k) + kv_first, L - key0, KB, kv_row_bytes);
 #pragma unroll
         for (int i = 0; i < KB * 16 / KT; ++i) {
             const int chunk_id = tid + KT * i;
@@ -405,7 +412,7 @@ __global__ __launch_bounds__(KT, 1) void tile_bwd_dkdv_bf16_d128(const BwdDkvPar
     bf16x8 vf[8];
     {
         const Rsrc vr = rows_rsrc(reinterpret_cast<const __bf16*>(p.v) + kv_first + (size_t)32 * wave * p.heads_kv * D,
-                                  L - kw0, kv_row_bytes);
+                                  L - kw0, 32, kv_row_bytes);
 #pragma unroll
         for (int c = 0; c < 8; ++c)
             vf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vr, r32 * kv_row_bytes + (16 * c + 8 * g) * 2, 0, 0));
@@ -444,8 +451,8 @@ __global__ __launch_bounds__(KT, 1) void tile_bwd_dkdv_bf16_d128(const BwdDkvPar
         const int s = kv_entry(p.sched, e_) >> 2;
         const int h = kv_head * G + hh_;
         const size_t first = ((size_t)(s * L + r0_) * p.heads_q + h) * D;
-        const u32x4 qd = rows_desc(reinterpret_cast<const __bf16*>(p.q) + first, L - r0_, q_row_bytes);
-        const u32x4 dd = rows_desc(reinterpret_cast<const __bf16*>(p.dout) + first, L - r0_, q_row_bytes);
+        const u32x4 qd = rows_desc(reinterpret_cast<const __bf16*>(p.q) + first, L - r0_, kRows, q_row_bytes);
+        const u32x4 dd = rows_desc(reinterpret_cast<const __bf16*>(p.dout) + first, L - r0_, kRows, q_row_bytes);
         const unsigned dst = stage0 + st * kStageBytes;
 #pragma unroll
         for (int i = 0; i < kStageDmaPerWave; ++i) {

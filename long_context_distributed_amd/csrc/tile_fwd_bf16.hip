@@ -84,11 +84,18 @@ static_assert(kWaveRowsBf16 == 32, "one 32-row block per wave");
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 #define LDS_AS __attribute__((address_space(3)))
 
-// Buffer resource over `rows` rows of `row_bytes` starting at base: loads
-// from rows at or past `rows` return zero, with no branch.
-__device__ __forceinline__ Rsrc rows_rsrc(const void* base, int rows, int row_bytes) {
-    const int n = rows > 0 ? (rows - 1) * row_bytes + D * 2 : 0;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcWord3);
+// Byte range of a descriptor that serves at most `max_rows` rows of
+// `row_bytes` from its base, of which `rows` exist: loads from rows at or past
+// `rows` return zero, with no branch.  Clamping to the rows actually read
+// keeps the range in 32 bits however long the partition is.
+__device__ __forceinline__ int rows_range(int rows, int max_rows, int row_bytes) {
+    const int r = rows < max_rows ? rows : max_rows;
+    return r > 0 ? (r - 1) * row_bytes + D * 2 : 0;
+}
+
+__device__ __forceinline__ Rsrc rows_rsrc(const void* base, int rows, int max_rows, int row_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                             rows_range(rows, max_rows, row_bytes), kRsrcWord3);
 }
 
 // Per-thread constants of the DMA loader and of the LDS reads.
@@ -124,9 +131,9 @@ __device__ __forceinline__ void init_lanes(Lanes& ln, int tid, int wave, int row
 }
 
 // Buffer descriptor words (base, range in bytes) for the DMA loads below.
-__device__ __forceinline__ u32x4 rows_desc(const void* base, int rows, int row_bytes) {
+__device__ __forceinline__ u32x4 rows_desc(const void* base, int rows, int max_rows, int row_bytes) {
     const unsigned long long a = reinterpret_cast<unsigned long long>(base);
-    const int n = rows > 0 ? (rows - 1) * row_bytes + D * 2 : 0;
+    const int n = rows_range(rows, max_rows, row_bytes);
     return u32x4{static_cast<unsigned>(a), static_cast<unsigned>(a >> 32) & 0xffffu,
                  static_cast<unsigned>(n), static_cast<unsigned>(kRsrcWord3)};
 }
@@ -254,7 +261,7 @@ __global__ __launch_bounds__(NT, 1) void tile_fwd_bf16_d128(const TileParams p) 
         const int qrow_bytes = p.heads_q * D * 2;
         const __bf16* q0 = reinterpret_cast<const __bf16*>(p.q) +
                            ((size_t)(w.q_slot * L + w.wave_tok0) * p.heads_q + w.head) * D;
-        const Rsrc qr = rows_rsrc(q0, L - w.wave_tok0, qrow_bytes);
+        const Rsrc qr = rows_rsrc(q0, L - w.wave_tok0, 32, qrow_bytes);
 #pragma unroll
         for (int c = 0; c < 8; ++c)
             qf[c] = __builtin_bit_cast(
@@ -294,7 +301,7 @@ __global__ __launch_bounds__(NT, 1) void tile_fwd_bf16_d128(const TileParams p) 
     const unsigned lds0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>((LDS_AS unsigned char*)smem));
     auto issue = [&](int bi_, int n0_, int buf_) {
         const size_t off = (size_t)(sched_entry(p.sched, bi_) >> 2) * slot_elems + (size_t)n0_ * p.heads_kv * D;
-        dma_tile(ln, rows_desc(kbase + off, L - n0_, row_bytes), rows_desc(vbase + off, L - n0_, row_bytes),
+        dma_tile(ln, rows_desc(kbase + off, L - n0_, BN, row_bytes), rows_desc(vbase + off, L - n0_, BN, row_bytes),
                  lds0 + buf_ * kBufBytes, wave);
     };
     auto vmcnt0_barrier = [&]() {

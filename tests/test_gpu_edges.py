@@ -128,3 +128,62 @@ def test_empty_block_list():
     mat.tile_bwd(q, k, v, do, lse_r, delta, [], w.part_len, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)
+
+
+@pytest.mark.timeout(600)
+def test_byte_ranges_past_32_bits():
+    """A partition whose token rows span more than 4 GiB of each tensor (1024
+    heads, L = 16449): every load's buffer range is clamped to the rows it
+    serves, so none wraps around 2^32.  Unclamped, the range of the tile that
+    starts at row 64 (2^14 + 1 rows left, 2^18 bytes each) would wrap to 256
+    bytes and rows 65..127 of Q, K and V would read as zero.  Forward and
+    backward, checked on rows and keys of the first tiles and at the end."""
+    import torch
+    import long_context_distributed_amd as mat
+    L, H, d = 16449, 1024, 128
+    say(f"[case] byte ranges past 32 bits: L={L}, {H} heads, d={d}")
+    scale = 1.0 / math.sqrt(d)
+    g = torch.Generator(device="cuda").manual_seed(21)
+    q, k, v, do = (torch.randn((L, H, d), generator=g, device="cuda", dtype=torch.bfloat16)
+                   for _ in range(4))
+    assert L * H * d * 2 > 2 ** 32
+    blocks = [(0, 0, 0, 0, mat.DIAG)]
+    o, lse = mat.tile_fwd(q, k, v, blocks, L, scale)
+    torch.cuda.synchronize()
+    pos = np.arange(L)
+    toks = np.array([0, 1, 63, 64, 65, 66, 95, 96, 127, 128, 200, L // 2, L - 2, L - 1])
+    heads = [0, 517, H - 1]
+    for h in heads:
+        sl = slice(h, h + 1)
+        rows = np.stack([toks, np.zeros_like(toks)], axis=1)
+        ref_o, ref_l = oracle.attention_ref(q[:, sl], k[:, sl], v[:, sl], pos, pos, True, scale,
+                                            rows=rows)
+        got_o = o[toks, h].float().cpu().numpy()
+        got_l = lse[toks, h].cpu().numpy()
+        e_o = float(np.max(np.abs(got_o - ref_o)))
+        e_l = float(np.max(np.abs(got_l - ref_l)))
+        say(f"[edge] >4 GiB rows, head {h}: max|dO|={e_o:.2e} max|dlse|={e_l:.2e}")
+        assert e_o <= 2e-2 and e_l <= 1e-3, (h, e_o, e_l)
+
+    # backward with the tile's own lse and D = rowsum(dO * O)
+    delta = mat.bwd_delta(o, do)
+    dq, dk, dv = mat.tile_bwd(q, k, v, do, lse, delta, blocks, L, scale)
+    torch.cuda.synchronize()
+    del o
+    keys = toks
+    for h in heads:
+        sl = slice(h, h + 1)
+        f64 = lambda t: t[:, sl].double().cpu().numpy()  # noqa: E731
+        qh, kh, vh, doh = f64(q), f64(k), f64(v), f64(do)
+        lh, dh = f64(lse), f64(delta)
+        ref_dq = oracle.attention_bwd_ref(qh[toks], kh, vh, doh[toks], lh[toks], dh[toks],
+                                          pos[toks], pos, True, scale)[0]
+        _, ref_dk, ref_dv = oracle.attention_bwd_ref(qh, kh[keys], vh[keys], doh, lh, dh, pos,
+                                                     pos[keys], True, scale)
+        for name, got, ref in (("dq", dq[toks, h], ref_dq[:, 0]), ("dk", dk[keys, h], ref_dk[:, 0]),
+                               ("dv", dv[keys, h], ref_dv[:, 0])):
+            got = got.cpu().numpy()
+            err = float(np.max(np.abs(got - ref)))
+            top = float(np.max(np.abs(ref)))
+            say(f"[edge] >4 GiB rows, head {h}: {name} max|err|={err:.2e} (max|ref| {top:.2e})")
+            assert err <= 2e-2 * top + 1e-6, (h, name, err, top)

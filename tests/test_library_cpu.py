@@ -113,6 +113,7 @@ INVALID_DESCS = {
     "scale nan": dict(softmax_scale=float("nan")),
     "scale inf": dict(softmax_scale=float("inf")),
     "head_dim zero": dict(head_dim=0),
+    "too many heads": dict(heads_q=4097 * 2, heads_kv=2),
     "tile too large": dict(part_len=1 << 30, n_q_slots=4),
 }
 
@@ -281,3 +282,12 @@ def test_calls_are_thread_safe(lib):
     for th in threads:
         th.join()
     assert not failures, failures[:5]
+
+
+def test_binding_constants_match_the_header():
+    """The limits the binding mirrors are the header's #defines."""
+    text = open(os.path.join(ROOT, "include", "mesh_attn.h")).read()
+    defines = dict(re.findall(r"#define MESH_ATTN_(MAX_\w+) (\d+)", text))
+    assert set(defines) == {"MAX_Q_SLOTS", "MAX_KV_SLOTS", "MAX_BLOCKS", "MAX_HEADS"}
+    for name, value in defines.items():
+        assert getattr(_lib, name) == int(value), name

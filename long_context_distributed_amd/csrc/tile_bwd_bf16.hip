@@ -267,7 +267,10 @@ __global__ __launch_bounds__(QT, 1) void tile_bwd_dq_bf16_d128(const BwdDqParams
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int key0 = n0 + 32 * h;
-                // S^T = K Q^T and dP^T = V dO^T for 32 keys.
+                // S^T = K Q^T and dP^T = V dO^T for 32 keys, at a raised wave
+                // priority so that the two MFMA chains issue ahead of the other
+                // wave's VALU work (measured: ~3% faster for this kernel).
+                __builtin_amdgcn_s_setprio(1);
                 f32x16 s, dp;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -280,6 +283,7 @@ __global__ __launch_bounds__(QT, 1) void tile_bwd_dq_bf16_d128(const BwdDqParams
                     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_b128(kt + kTileBytes + to.row[c] + 8192 * h),
                                                                  dof[c], dp, 0, 0, 0);
                 }
+                __builtin_amdgcn_s_setprio(0);
                 if ((dg && key0 + 31 > w.wave_tok0) || key0 + 32 > L) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {

@@ -345,12 +345,17 @@ __global__ __launch_bounds__(NT, 1) void tile_fwd_bf16_d128(const TileParams p) 
         auto step = [&](auto h_tag, const LDS_AS unsigned char* cur, const LDS_AS unsigned char* nxt,
                         bool mask_next, bool diag_next, int key0_next) {
             constexpr int H = decltype(h_tag)::value;
-            // QK^T of the next half with the exponentials of this half.
+            // QK^T of the next half with the exponentials of this half, at a
+            // raised wave priority: the SIMD's arbiter then favours the wave
+            // whose dependent QK chain is waiting to issue over the other two
+            // waves' softmax and PV work (measured: ~1% faster than no priority).
+            __builtin_amdgcn_s_setprio(1);
             f32x16 s_next = qk_half(ln, qf, nxt, H ^ 1);
             bf16x8 pb[2];
             softmax_half(s, c2, m, l, pb);
             // Keep the softmax here (not sunk past the mask branch to the PV).
             asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(l));
+            __builtin_amdgcn_s_setprio(0);
             if (mask_next) mask_half(s_next, key0_next, L, diag_next, u);
             // PV of this half with the maximum of the next half.
             const float m_cand = row_max(s_next) * c2;

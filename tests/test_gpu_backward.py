@@ -40,6 +40,8 @@ CASES = [
     (96, (3, 2), (1, 0), False, False, 6, 2),    # non-causal, G=3
     (300, (2, 4), (1, 2), True, True, 16, 2),    # G=8, two head groups, two key blocks
     (520, (2, 2), (1, 0), True, True, 4, 1),     # nine 64-key tiles per block, three key blocks
+    (100, (2, 2), (1, 0), True, True, 12, 1),    # G=12
+    (70, (2, 3), (0, 2), True, True, 10, 2),     # G=5
 ]
 
 

@@ -109,7 +109,8 @@ def test_deterministic_and_canaries():
 @pytest.mark.parametrize("dtype,d,n", [("bf16", 128, 5), ("f32", 64, 5), ("bf16", 64, 5),
                                        ("f32", 128, 5), ("bf16", 128, 1), ("bf16", 128, 2),
                                        ("bf16", 128, 16), ("bf16", 128, 20), ("f32", 64, 33),
-                                       ("bf16", 24, 3), ("f32", 12, 7)])
+                                       ("bf16", 24, 3), ("f32", 12, 7), ("bf16", 128, 64),
+                                       ("f32", 128, 64)])
 def test_merge_matches_oracle(dtype, d, n):
     import torch
     import long_context_distributed_amd as mat

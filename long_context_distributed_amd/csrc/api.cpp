@@ -182,6 +182,57 @@ static void set_row_decomposition(Params& p, const mesh_attn_tile_desc& d, int w
 
 using namespace mesh_attn;
 
+namespace mesh_attn {
+
+int plan_tile_fwd(const char* who, const mesh_attn_tile_desc& d, TileParams& p) {
+    const int shape_st = check_tile_shape(who, d);
+    if (shape_st != MESH_ATTN_OK) return shape_st;
+    const bool supported = (d.dtype == MESH_ATTN_BF16 && d.head_dim == 128) ||
+                           (d.dtype == MESH_ATTN_F32 && (d.head_dim == 64 || d.head_dim == 128));
+    if (!supported)
+        return failw(MESH_ATTN_ERR_UNSUPPORTED, who, "dtype/head_dim combination not built");
+
+    memset(&p, 0, sizeof(p));
+    const int st = build_schedule(who, d, p.sched, nullptr);
+    if (st != MESH_ATTN_OK) return st;
+    set_row_decomposition(p, d, d.dtype == MESH_ATTN_BF16 ? kTileWavesBf16 : kTileWavesF32,
+                          d.dtype == MESH_ATTN_BF16 ? kWaveRowsBf16 : kWaveRowsF32);
+    p.scale_log2e = d.softmax_scale * 1.4426950408889634f;
+    if (tile_fwd_grid(p) > INT32_MAX) return failw(MESH_ATTN_ERR_INVALID, who, "grid too large");
+    return MESH_ATTN_OK;
+}
+
+int plan_tile_bwd(const char* who, const mesh_attn_tile_desc& d, BwdDqParams& pq, BwdDkvParams& pk) {
+    const int shape_st = check_tile_shape(who, d);
+    if (shape_st != MESH_ATTN_OK) return shape_st;
+    if (!(d.dtype == MESH_ATTN_BF16 && d.head_dim == 128))
+        return failw(MESH_ATTN_ERR_UNSUPPORTED, who, "dtype/head_dim combination not built");
+
+    memset(&pq, 0, sizeof(pq));
+    memset(&pk, 0, sizeof(pk));
+    const int st = build_schedule(who, d, pq.sched, &pk.sched);
+    if (st != MESH_ATTN_OK) return st;
+
+    set_row_decomposition(pq, d, kBwdDqWaves, kBwdRowsPerWave);
+    pq.scale = d.softmax_scale;
+    pq.scale_log2e = d.softmax_scale * 1.4426950408889634f;
+
+    pk.part_len = d.part_len;
+    pk.heads_q = d.heads_q;
+    pk.heads_kv = d.heads_kv;
+    pk.group = d.heads_q / d.heads_kv;
+    pk.n_kv_slots = d.n_kv_slots;
+    const int keys_per_wg = kBwdDkvWaves * kBwdRowsPerWave;
+    pk.n_key_blocks = (d.part_len + keys_per_wg - 1) / keys_per_wg;
+    pk.scale = pq.scale;
+    pk.scale_log2e = pq.scale_log2e;
+    if (tile_fwd_grid(pq) > INT32_MAX || tile_bwd_dkdv_grid(pk) > INT32_MAX)
+        return failw(MESH_ATTN_ERR_INVALID, who, "grid too large");
+    return MESH_ATTN_OK;
+}
+
+}  // namespace mesh_attn
+
 extern "C" int mesh_attn_tile_fwd(const mesh_attn_tile_desc* desc, const void* q, const void* k,
                                   const void* v, void* o, float* lse, void* hip_stream) {
     const char* who = "tile_fwd";
@@ -191,30 +242,14 @@ extern "C" int mesh_attn_tile_fwd(const mesh_attn_tile_desc* desc, const void* q
         return failw(MESH_ATTN_ERR_INVALID, who, "NULL tensor pointer");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
         return failw(MESH_ATTN_ERR_INVALID, who, "tensor pointer not 16-byte aligned");
-    const int shape_st = check_tile_shape(who, d);
-    if (shape_st != MESH_ATTN_OK) return shape_st;
-    const bool supported = (d.dtype == MESH_ATTN_BF16 && d.head_dim == 128) ||
-                           (d.dtype == MESH_ATTN_F32 && (d.head_dim == 64 || d.head_dim == 128));
-    if (!supported)
-        return failw(MESH_ATTN_ERR_UNSUPPORTED, who, "dtype/head_dim combination not built");
-
     TileParams p;
-    memset(&p, 0, sizeof(p));
-    const int st = build_schedule(who, d, p.sched, nullptr);
+    const int st = plan_tile_fwd(who, d, p);
     if (st != MESH_ATTN_OK) return st;
-
     p.q = q;
     p.k = k;
     p.v = v;
     p.o = o;
     p.lse = lse;
-    set_row_decomposition(p, d, d.dtype == MESH_ATTN_BF16 ? kTileWavesBf16 : kTileWavesF32,
-                          d.dtype == MESH_ATTN_BF16 ? kWaveRowsBf16 : kWaveRowsF32);
-    p.scale_log2e = d.softmax_scale * 1.4426950408889634f;
-
-    const int64_t n_wg = static_cast<int64_t>(d.n_q_slots) * p.n_tok_blocks * d.heads_kv *
-                         p.n_head_groups;
-    if (n_wg > INT32_MAX) return failw(MESH_ATTN_ERR_INVALID, who, "grid too large");
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     const hipError_t e = d.dtype == MESH_ATTN_BF16 ? launch_tile_fwd_bf16(p, d.head_dim, stream)
@@ -304,19 +339,10 @@ extern "C" int mesh_attn_tile_bwd(const mesh_attn_tile_desc* desc, const void* q
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(lse) ||
         !aligned16(delta) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
         return failw(MESH_ATTN_ERR_INVALID, who, "tensor pointer not 16-byte aligned");
-    const int shape_st = check_tile_shape(who, d);
-    if (shape_st != MESH_ATTN_OK) return shape_st;
-    if (!(d.dtype == MESH_ATTN_BF16 && d.head_dim == 128))
-        return failw(MESH_ATTN_ERR_UNSUPPORTED, who, "dtype/head_dim combination not built");
-
     BwdDqParams pq;
     BwdDkvParams pk;
-    memset(&pq, 0, sizeof(pq));
-    memset(&pk, 0, sizeof(pk));
-    const int st = build_schedule(who, d, pq.sched, &pk.sched);
+    const int st = plan_tile_bwd(who, d, pq, pk);
     if (st != MESH_ATTN_OK) return st;
-
-    set_row_decomposition(pq, d, kBwdDqWaves, kBwdRowsPerWave);
     pq.q = q;
     pq.k = k;
     pq.v = v;
@@ -324,9 +350,6 @@ extern "C" int mesh_attn_tile_bwd(const mesh_attn_tile_desc* desc, const void* q
     pq.lse = lse;
     pq.delta = delta;
     pq.dq = dq;
-    pq.scale = d.softmax_scale;
-    pq.scale_log2e = d.softmax_scale * 1.4426950408889634f;
-
     pk.q = q;
     pk.k = k;
     pk.v = v;
@@ -335,21 +358,6 @@ extern "C" int mesh_attn_tile_bwd(const mesh_attn_tile_desc* desc, const void* q
     pk.delta = delta;
     pk.dk = dk;
     pk.dv = dv;
-    pk.part_len = d.part_len;
-    pk.heads_q = d.heads_q;
-    pk.heads_kv = d.heads_kv;
-    pk.group = d.heads_q / d.heads_kv;
-    pk.n_kv_slots = d.n_kv_slots;
-    const int keys_per_wg = kBwdDkvWaves * kBwdRowsPerWave;
-    pk.n_key_blocks = (d.part_len + keys_per_wg - 1) / keys_per_wg;
-    pk.scale = pq.scale;
-    pk.scale_log2e = pq.scale_log2e;
-
-    const int64_t n_wg_q = static_cast<int64_t>(d.n_q_slots) * pq.n_tok_blocks * d.heads_kv *
-                           pq.n_head_groups;
-    const int64_t n_wg_k = static_cast<int64_t>(d.n_kv_slots) * pk.n_key_blocks * d.heads_kv;
-    if (n_wg_q > INT32_MAX || n_wg_k > INT32_MAX)
-        return failw(MESH_ATTN_ERR_INVALID, who, "grid too large");
 
     const hipError_t e = launch_tile_bwd_bf16(pq, pk, d.head_dim, static_cast<hipStream_t>(hip_stream));
     return hip_status(e, "tile_bwd: kernel launch failed");

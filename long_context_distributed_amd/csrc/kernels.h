@@ -7,6 +7,8 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include "mesh_attn.h"
+
 namespace mesh_attn {
 
 constexpr int kMaxQSlots = 64;
@@ -31,7 +33,7 @@ struct TileSchedule {
 
 // Entry i of the packed schedule, read as a dword so that a wave-uniform
 // index becomes a scalar load (there are no scalar byte loads on gfx9).
-__device__ __forceinline__ int sched_entry(const TileSchedule& s, int i) {
+__host__ __device__ __forceinline__ int sched_entry(const TileSchedule& s, int i) {
     const uint32_t word = reinterpret_cast<const uint32_t*>(s.blk)[i >> 2];
     return (word >> (8 * (i & 3))) & 0xff;
 }
@@ -135,6 +137,22 @@ static_assert(offsetof(BwdDkvParams, sched) % 4 == 0, "schedule must be dword al
 constexpr int kBwdDqWaves = 8;
 constexpr int kBwdDkvWaves = 8;
 constexpr int kBwdRowsPerWave = 32;
+
+// Workgroups of a forward-decomposed launch (tile forward, query-gradient
+// kernel) and of the key/value-gradient kernel.
+template <typename Params>
+inline int64_t tile_fwd_grid(const Params& p) {
+    return static_cast<int64_t>(p.n_q_slots) * p.n_tok_blocks * p.heads_kv * p.n_head_groups;
+}
+inline int64_t tile_bwd_dkdv_grid(const BwdDkvParams& p) {
+    return static_cast<int64_t>(p.n_kv_slots) * p.n_key_blocks * p.heads_kv;
+}
+
+// Host planning of a tile call: validates the description, packs the
+// schedule and sets the work decomposition (tensor pointers are left NULL).
+// Returns a status; the entry points launch what these produce.
+int plan_tile_fwd(const char* who, const mesh_attn_tile_desc& d, TileParams& p);
+int plan_tile_bwd(const char* who, const mesh_attn_tile_desc& d, BwdDqParams& pq, BwdDkvParams& pk);
 
 hipError_t launch_tile_fwd_bf16(const TileParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_tile_fwd_f32(const TileParams& p, int head_dim, hipStream_t stream);

@@ -370,11 +370,10 @@ __global__ __launch_bounds__(KT, 1) void tile_bwd_dkdv_bf16_d128(const BwdDkvPar
     const int g = lane >> 5, r32 = lane & 31;
     const int L = p.part_len;
     const int G = p.group;
-    int lam = blockIdx.x;
-    const int kv_head = lam % p.heads_kv;
-    lam /= p.heads_kv;
-    const int kb = lam % p.n_key_blocks;
-    const int kv_slot = lam / p.n_key_blocks;
+    const dev::KeyBlock kbk = dev::decode_key_block_at(p, static_cast<int>(blockIdx.x));
+    const int kv_head = kbk.kv_head;
+    const int kb = kbk.key_block;
+    const int kv_slot = kbk.kv_slot;
     const int key0 = kb * KB;               // first key of the workgroup (partition offset)
     const int kw0 = key0 + 32 * wave;       // first key of this wave
     const int key = kw0 + r32;              // this lane's key
@@ -568,12 +567,11 @@ __global__ __launch_bounds__(KT, 1) void tile_bwd_dkdv_bf16_d128(const BwdDkvPar
 hipError_t launch_tile_bwd_bf16(const BwdDqParams& pq, const BwdDkvParams& pk, int head_dim,
                                hipStream_t stream) {
     if (head_dim != D || pq.wave_rows != kBwdRowsPerWave) return hipErrorInvalidValue;
-    const unsigned n_wg_q = static_cast<unsigned>(pq.n_q_slots) * pq.n_tok_blocks * pq.heads_kv *
-                            pq.n_head_groups;
+    const unsigned n_wg_q = static_cast<unsigned>(tile_fwd_grid(pq));
     hipLaunchKernelGGL(tile_bwd_dq_bf16_d128, dim3(n_wg_q), dim3(QT), 0, stream, pq);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const unsigned n_wg_k = static_cast<unsigned>(pk.n_kv_slots) * pk.n_key_blocks * pk.heads_kv;
+    const unsigned n_wg_k = static_cast<unsigned>(tile_bwd_dkdv_grid(pk));
     hipLaunchKernelGGL(tile_bwd_dkdv_bf16_d128, dim3(n_wg_k), dim3(KT), 0, stream, pk);
     return hipGetLastError();
 }

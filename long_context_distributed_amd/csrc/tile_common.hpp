@@ -44,14 +44,14 @@ struct WorkItem {
     int wg_tok_end;  // one past the workgroup's last valid token (<= L)
 };
 
-// blockIdx.x -> work item.  KV head varies fastest, then query-head group,
-// then token block (highest first: in a DIAG block later tokens see more
-// keys), then Q slot in heaviest-first order.
-// Works for every parameter struct with the forward's decomposition fields
-// (TileParams, BwdDqParams).
+// Workgroup index -> work item.  KV head varies fastest, then query-head
+// group, then token block (highest first: in a DIAG block later tokens see
+// more keys), then Q slot in heaviest-first order.  Works for every
+// parameter struct with the forward's decomposition fields (TileParams,
+// BwdDqParams); callable on the host so that the grid's coverage can be
+// checked there.
 template <typename Params>
-__device__ __forceinline__ WorkItem decode_work(const Params& p, int wave) {
-    int lam = blockIdx.x;
+__host__ __device__ inline WorkItem decode_work_at(const Params& p, int lam, int wave) {
     WorkItem w;
     w.kv_head = lam % p.heads_kv;
     lam /= p.heads_kv;
@@ -66,8 +66,32 @@ __device__ __forceinline__ WorkItem decode_work(const Params& p, int wave) {
     w.head = w.kv_head * p.group + hg * p.heads_per_wg + h_in;
     w.wg_tok0 = tb * p.wave_rows * p.tok_groups;
     w.wave_tok0 = w.wg_tok0 + p.wave_rows * tg;
-    w.wg_tok_end = min(p.part_len, w.wg_tok0 + p.wave_rows * p.tok_groups);
+    const int wg_end = w.wg_tok0 + p.wave_rows * p.tok_groups;
+    w.wg_tok_end = wg_end < p.part_len ? wg_end : p.part_len;
     return w;
+}
+
+template <typename Params>
+__device__ __forceinline__ WorkItem decode_work(const Params& p, int wave) {
+    return decode_work_at(p, static_cast<int>(blockIdx.x), wave);
+}
+
+// Workgroup index of the key/value-gradient kernel -> (KV slot, key block,
+// KV head); the KV head varies fastest.
+struct KeyBlock {
+    int kv_slot;
+    int key_block;
+    int kv_head;
+};
+
+template <typename Params>
+__host__ __device__ inline KeyBlock decode_key_block_at(const Params& p, int lam) {
+    KeyBlock b;
+    b.kv_head = lam % p.heads_kv;
+    lam /= p.heads_kv;
+    b.key_block = lam % p.n_key_blocks;
+    b.kv_slot = lam / p.n_key_blocks;
+    return b;
 }
 
 }  // namespace dev

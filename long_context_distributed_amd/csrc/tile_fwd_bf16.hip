@@ -418,8 +418,7 @@ __global__ __launch_bounds__(NT, 1) void tile_fwd_bf16_d128(const TileParams p) 
 
 hipError_t launch_tile_fwd_bf16(const TileParams& p, int head_dim, hipStream_t stream) {
     if (head_dim != D || p.wave_rows != kWaveRowsBf16) return hipErrorInvalidValue;
-    const unsigned n_wg = static_cast<unsigned>(p.n_q_slots) * p.n_tok_blocks * p.heads_kv *
-                          p.n_head_groups;
+    const unsigned n_wg = static_cast<unsigned>(tile_fwd_grid(p));
     hipLaunchKernelGGL(tile_fwd_bf16_d128, dim3(n_wg), dim3(NT), 0, stream, p);
     return hipGetLastError();
 }

@@ -166,8 +166,7 @@ __global__ __launch_bounds__(NT, 2) void tile_fwd_f32_kernel(const TileParams p)
 }  // namespace
 
 hipError_t launch_tile_fwd_f32(const TileParams& p, int head_dim, hipStream_t stream) {
-    const unsigned n_wg = static_cast<unsigned>(p.n_q_slots) * p.n_tok_blocks * p.heads_kv *
-                          p.n_head_groups;
+    const unsigned n_wg = static_cast<unsigned>(tile_fwd_grid(p));
     if (head_dim == 64)
         hipLaunchKernelGGL(tile_fwd_f32_kernel<64>, dim3(n_wg), dim3(NT), 0, stream, p);
     else if (head_dim == 128)

@@ -374,6 +374,10 @@ def main():
                      "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE)",
                      "kernel": tile_kernel},
     }
+    props = torch.cuda.get_device_properties(dev)
+    result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                        "compute_units": props.multi_processor_count,
+                        "memory_gib": round(props.total_memory / 2 ** 30, 1)}
     if a.backward_steps > 0 and w.dtype == "bf16":
         result["tile_bwd"] = backward_leg(a.backward_steps, a.workload, w, q, k, v, o_own, l_own,
                                           q_parts, blocks, flops, dev)

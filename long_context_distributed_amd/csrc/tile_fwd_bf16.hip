@@ -65,7 +65,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4_raw __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;      // head dim
 constexpr int BN = 64;      // keys per LDS tile

@@ -374,6 +374,20 @@ def main():
                      "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE)",
                      "kernel": tile_kernel},
     }
+    # Row a1 (host): the block list of this tile, library call against the oracle's brute force.
+    t0 = time.perf_counter()
+    for _ in range(1000):
+        mat.block_list(R, C, r, c, w.causal, w.kv_rotate)
+    bl_us = (time.perf_counter() - t0) * 1e3
+    result["block_list"] = {"us": bl_us, "blocks": len(blocks),
+                            "note": "host call through the Python binding, mean of 1000"}
+    if not a.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        for _ in range(20):
+            ref_bl = oracle.block_list_ref(R, C, r, c, w.causal, w.kv_rotate)
+        result["block_list"]["oracle_us"] = (time.perf_counter() - t0) / 20 * 1e6
+        result["block_list"]["equal_to_oracle"] = ref_bl == blocks
     props = torch.cuda.get_device_properties(dev)
     result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                         "compute_units": props.multi_processor_count,

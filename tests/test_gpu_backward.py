@@ -42,6 +42,7 @@ CASES = [
     (520, (2, 2), (1, 0), True, True, 4, 1),     # nine 64-key tiles per block, three key blocks
     (100, (2, 2), (1, 0), True, True, 12, 1),    # G=12
     (70, (2, 3), (0, 2), True, True, 10, 2),     # G=5
+    (90, (4, 2), (2, 1), True, False, 4, 2),     # causal with contiguous KV order
 ]
 
 

@@ -28,6 +28,7 @@ SMALL = [
     ("bf16", 200, (2, 4), (1, 2), True, True, 16, 2, 128),   # G=8 with 2 head groups
     ("bf16", 100, (2, 2), (1, 0), True, True, 12, 1, 128),   # G=12: all 12 waves on heads of one group
     ("bf16", 70, (2, 3), (0, 2), True, True, 10, 2, 128),    # G=5: one head per workgroup, 5 head groups
+    ("bf16", 90, (4, 2), (2, 1), True, False, 4, 2, 128),    # causal with contiguous KV order
     ("f32", 64, (2, 2), (0, 0), False, False, 1, 1, 64),
     ("f32", 33, (2, 2), (1, 1), True, True, 2, 1, 64),
     ("f32", 40, (4, 2), (2, 1), True, True, 4, 2, 128),

@@ -13,12 +13,24 @@ tests check.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
                     [--backward-steps N] [--no-cpu-baseline] [--copy-calibration MIB]
+                    [--others none|all|1,2,...]
 
 After the forward steps, --backward-steps N (default 3, 0 = off; bf16 tiles)
 times the tile backward on the same tile: the row-term kernel D = rowsum(dO*O)
 and the dQ and dK/dV kernels, reported in "tile_bwd" (not part of "value").
 The rows' lse and O are this tile's own forward results, which have the shapes
 and value ranges of the final ones; dO is synthetic.
+
+--others (default "all") then measures the other workloads the same way, each
+with fewer steps and a shorter oracle sample, under "per_workload" (the
+headline workload is repeated there, so the table holds all five).  The
+headline "value" is always the --workload tile.
+
+The merge's byte count follows what the kernel reads: every partial's lse,
+the output rows of the partials whose lse is finite (a partial that saw no
+key for a row is not read), and the merged row it writes.  "gbs" and
+"frac_hbm" use that count; "bytes_all_rows" is the count if every partial
+row were read.
 
 --copy-calibration runs one plain device copy of MIB MiB after the steps, so
 that a hardware-counter run can scale FETCH_SIZE / WRITE_SIZE by what they
@@ -113,8 +125,16 @@ def tile_flops(blocks, part_len, heads_q, head_dim):
 
 
 def merge_bytes(n, rows, d, elt):
-    """Algorithmic bytes of one merge: read n partial rows (O and lse), write one."""
+    """Algorithmic bytes of one merge if every partial row is read: n partial
+    rows (O and lse) read, one written."""
     return n * rows * (d * elt + 4) + rows * (d * elt + 4)
+
+
+def merge_live_bytes(n, rows, d, elt, live):
+    """Bytes the merge moves when the output rows of dead partials (lse =
+    -inf, `live` of the n*rows are finite) are not read: every lse, the live
+    output rows, and the merged row with its lse."""
+    return n * rows * 4 + live * d * elt + rows * (d * elt + 4)
 
 
 def _oracle_rows_rate(w, qh, kh, vh, qpos, kpos, rows_all, budget_s):
@@ -235,39 +255,68 @@ def backward_leg(steps, wid, w, q, k, v, o, lse, q_parts, blocks, fwd_flops, dev
                           "gbs": dbytes / (t_delta * 1e-3) / 1e9}}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--backward-steps", type=int, default=3)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
-    a = ap.parse_args()
-    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's tile only: the hot path is one GPU's share of the "
-              "mesh and this build has no multi-GPU path; run it with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+def peer_kv_sets(w, block_list):
+    """KV partitions behind each partial the merge combines: the mesh-row
+    sibling tiles' KV sets, or (the per-KV-partition merge) one partition
+    each.  block_list(R, C, r, c, causal, rotate) gives a tile's blocks."""
+    R, C, r, c = w.mesh_rows, w.mesh_cols, w.tile_row, w.tile_col
+    if w.merge == "per_kv_part":
+        kv = [b[3] for b in block_list(R, C, r, c, w.causal, w.kv_rotate) if b[0] == 0]
+        return [[kp] for kp in kv], None
+    sets = []
+    for i in range(C):
+        sb = block_list(R, C, r, i, w.causal, w.kv_rotate)
+        sets.append([b[3] for b in sb if b[0] == 0])
+    return sets, c
 
+
+def dead_partials(w, q_parts, peer_kv):
+    """dead[i][s]: partial i holds no key visible to Q slot s (lse = -inf on
+    all of the slot's rows), i.e. none of its KV partitions is at or before
+    the slot's partition (causal only)."""
+    return [[w.causal and not any(kp <= qp for kp in kvp) for qp in q_parts] for kvp in peer_kv]
+
+
+def live_partial_rows(w, q_parts, peer_kv):
+    """Partial rows with a finite lse: the rows the merge reads outputs of."""
+    dead = dead_partials(w, q_parts, peer_kv)
+    return sum(w.part_len * w.heads_q for row in dead for x in row if not x)
+
+
+def _peer_partials(w, mat, q_parts, n_tok, rows, d, dtype, dev):
+    """Partials the peers would return: same shapes, random outputs, finite
+    lse, and -inf where the peer's tile holds no KV partition at or before
+    the row's partition.  Returns (o_parts, l_parts, own index or None)."""
+    import torch
+    peer_kv, own = peer_kv_sets(w, mat.block_list)
+    n_parts = len(peer_kv)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    o_parts = (0.05 * torch.randn((n_parts, rows, d), generator=gen, device=dev)).to(dtype)
+    l_parts = 10.0 + torch.randn((n_parts, rows), generator=gen, device=dev)
+    for i, row in enumerate(dead_partials(w, q_parts, peer_kv)):
+        for s_, dead in enumerate(row):
+            if dead:
+                l_parts[i].view(n_tok, w.heads_q)[s_ * w.part_len:(s_ + 1) * w.part_len] = -math.inf
+    return o_parts, l_parts, own
+
+
+def measure_workload(wid, steps, warmup, backward_steps, cpu_budget, copy_calibration, dev):
+    """Times whole steps (block list + tile forward + merge) of one workload,
+    with per-kernel HIP events on the launch stream, then the backward, then
+    the oracle on host cores.  Returns (result dict, step ms)."""
     import torch
     import long_context_distributed_amd as mat
     import workloads
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a HIP GPU", file=sys.stderr)
-        sys.exit(2)
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    w = workloads.WORKLOADS[a.workload]
+    w = workloads.WORKLOADS[wid]
     scale = 1.0 / math.sqrt(w.head_dim)
     R, C, r, c = w.mesh_rows, w.mesh_cols, w.tile_row, w.tile_col
 
     blocks = mat.block_list(R, C, r, c, w.causal, w.kv_rotate)
     q_parts = [b[2] for b in blocks if b[1] == 0]
     kv_parts = [b[3] for b in blocks if b[0] == 0]
-    log(f"[bench] workload {a.workload}: {w.name}")
+    log(f"[bench] workload {wid}: {w.name}")
     q = workloads.gather(w, "q", q_parts, dev)
     k = workloads.gather(w, "k", kv_parts, dev)
     v = workloads.gather(w, "v", kv_parts, dev)
@@ -275,25 +324,8 @@ def main():
     rows = n_tok * w.heads_q
     elt = 2 if w.dtype == "bf16" else 4
 
-    # Partials the peers would return: same shapes, -inf where the peer's
-    # tile holds no KV partition at or before the row's partition.
-    if w.merge == "per_kv_part":
-        n_parts, own = R, None
-        peer_kv = [[kp] for kp in kv_parts]
-    else:
-        n_parts, own = C, c
-        peer_kv = []
-        for i in range(C):
-            sb = mat.block_list(R, C, r, i, w.causal, w.kv_rotate)
-            peer_kv.append([b[3] for b in sb if b[0] == 0])
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(11)
-    o_parts = (0.05 * torch.randn((n_parts, rows, d), generator=gen, device=dev)).to(q.dtype)
-    l_parts = 10.0 + torch.randn((n_parts, rows), generator=gen, device=dev)
-    for i, kvp in enumerate(peer_kv):
-        for s_, qp in enumerate(q_parts):
-            if w.causal and not any(kp <= qp for kp in kvp):
-                l_parts[i].view(n_tok, w.heads_q)[s_ * w.part_len:(s_ + 1) * w.part_len] = -math.inf
+    o_parts, l_parts, own = _peer_partials(w, mat, q_parts, n_tok, rows, d, q.dtype, dev)
+    n_parts = o_parts.shape[0]
     if own is not None:
         o_own, l_own = o_parts[own].view_as(q), l_parts[own].view(n_tok, w.heads_q)
     else:
@@ -304,10 +336,10 @@ def main():
     torch.cuda.synchronize()
 
     flops = tile_flops(blocks, w.part_len, w.heads_q, d)
-    mbytes = merge_bytes(n_parts, rows, d, elt)
-    # Bytes when dead partial rows (lse = -inf) are not read, as the kernel does.
+    mbytes_all = merge_bytes(n_parts, rows, d, elt)
     live = int(torch.isfinite(l_parts).sum().item())
-    mbytes_live = n_parts * rows * 4 + live * d * elt + rows * (d * elt + 4)
+    assert live == live_partial_rows(w, q_parts, peer_kv_sets(w, mat.block_list)[0])
+    mbytes = merge_live_bytes(n_parts, rows, d, elt, live)
 
     ev = []
 
@@ -326,15 +358,15 @@ def main():
             e2.record()
             ev.append((e0, e1, e2))
 
-    for _ in range(a.warmup):
+    for _ in range(warmup):
         step(False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(a.steps):
+    for _ in range(steps):
         step(True)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_step = 1e3 * elapsed / a.steps
+    ms_step = 1e3 * elapsed / steps
     t_tile = sum(e0.elapsed_time(e1) for e0, e1, _ in ev) / len(ev)   # ms
     t_merge = sum(e1.elapsed_time(e2) for _, e1, e2 in ev) / len(ev)  # ms
     tile_tflops = flops / (t_tile * 1e-3) / 1e12
@@ -343,11 +375,104 @@ def main():
     tile_kernel = "tile_fwd_bf16_d128" if w.dtype == "bf16" else "tile_fwd_f32"
     log(f"[bench] tile {t_tile:.3f} ms = {tile_tflops:.1f} TFLOP/s ({100 * tile_tflops / peak:.1f}% "
         f"of {peak}); merge {t_merge:.3f} ms = {merge_gbs:.0f} GB/s "
-        f"({100 * merge_gbs / PEAK_HBM_GBS:.1f}% of HBM); step {ms_step:.3f} ms")
+        f"({100 * merge_gbs / PEAK_HBM_GBS:.1f}% of HBM, {mbytes / 1e9:.3f} GB read+written); "
+        f"step {ms_step:.3f} ms")
 
+    res = {
+        "workload": wid,
+        "dtype": w.dtype,
+        "config": {"workload": w.name, "mesh": f"{R}x{C}", "tile": [r, c],
+                   "part_len": w.part_len, "q_tokens": n_tok, "kv_tokens": k.shape[0],
+                   "heads_q": w.heads_q, "heads_kv": w.heads_kv, "head_dim": d,
+                   "causal": w.causal, "kv_rotate": w.kv_rotate, "merge_partials": n_parts,
+                   "parallelism": "one GPU's tile"},
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_step,
+        "step_tflops": flops / (ms_step * 1e-3) / 1e12,
+        "tile_fwd": {"ms": t_tile, "tflops": tile_tflops, "frac_peak": tile_tflops / peak,
+                     "peak": peak, "flops": flops, "kernel": tile_kernel,
+                     "traffic": measured_traffic(tile_kernel, wid)},
+        "lse_merge": {"ms": t_merge, "gbs": merge_gbs, "frac_hbm": merge_gbs / PEAK_HBM_GBS,
+                      "bytes": mbytes, "bytes_all_rows": mbytes_all,
+                      "live_partial_rows": live, "partial_rows": n_parts * rows,
+                      "traffic": measured_traffic("lse_merge_kernel", wid)},
+    }
+    # Row a1 (host): the block list of this tile, library call against the oracle's brute force.
+    t0 = time.perf_counter()
+    for _ in range(1000):
+        mat.block_list(R, C, r, c, w.causal, w.kv_rotate)
+    bl_us = (time.perf_counter() - t0) * 1e3
+    res["block_list"] = {"us": bl_us, "blocks": len(blocks),
+                         "note": "host call through the Python binding, mean of 1000"}
+    if cpu_budget > 0:
+        import oracle
+        t0 = time.perf_counter()
+        for _ in range(20):
+            ref_bl = oracle.block_list_ref(R, C, r, c, w.causal, w.kv_rotate)
+        res["block_list"]["oracle_us"] = (time.perf_counter() - t0) / 20 * 1e6
+        res["block_list"]["equal_to_oracle"] = ref_bl == blocks
+    if backward_steps > 0 and w.dtype == "bf16":
+        res["tile_bwd"] = backward_leg(backward_steps, wid, w, q, k, v, o_own, l_own,
+                                       q_parts, blocks, flops, dev)
+    if copy_calibration > 0:
+        src = torch.empty(copy_calibration << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] copy calibration: {copy_calibration} MiB read + written by one copy kernel")
+    if cpu_budget > 0:
+        log(f"[bench] timing the oracle on host cores ({cpu_budget:.0f} s budget)")
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, q_parts, kv_parts, flops, o_parts,
+                                           l_parts, cpu_budget)
+    del q, k, v, o_parts, l_parts, o_own, l_own, o_m, l_m
+    torch.cuda.empty_cache()
+    return res, ms_step
+
+
+def _others(spec):
+    if spec == "none":
+        return []
+    if spec == "all":
+        return [1, 2, 3, 4, 5]
+    return sorted({int(x) for x in spec.split(",") if x.strip()})
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--backward-steps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    ap.add_argument("--others", default="all",
+                    help="other workloads measured after the headline: none, all or a list")
+    ap.add_argument("--others-steps", type=int, default=5)
+    ap.add_argument("--others-cpu-budget", type=float, default=5.0)
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's tile only: the hot path is one GPU's share of the "
+              "mesh and this build has no multi-GPU path; run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cpu_budget = 0.0 if a.no_cpu_baseline else a.cpu_budget
+    head, ms_step = measure_workload(a.workload, a.steps, a.warmup, a.backward_steps, cpu_budget,
+                                     a.copy_calibration, dev)
+    tf = head["tile_fwd"]
     result = {
         "metric": METRIC,
-        "value": flops / (ms_step * 1e-3) / 1e12,
+        "value": head["step_tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": a.steps,
@@ -356,55 +481,35 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": head["dtype"],
         "data": "synthetic",
-        "config": {"workload": w.name, "mesh": f"{R}x{C}", "tile": [r, c],
-                   "part_len": w.part_len, "q_tokens": n_tok, "kv_tokens": k.shape[0],
-                   "heads_q": w.heads_q, "heads_kv": w.heads_kv, "head_dim": d,
-                   "causal": w.causal, "kv_rotate": w.kv_rotate, "merge_partials": n_parts,
-                   "parallelism": "one GPU's tile"},
-        "tile_fwd": {"ms": t_tile, "tflops": tile_tflops, "frac_peak": tile_tflops / peak,
-                     "flops": flops},
-        "lse_merge": {"ms": t_merge, "gbs": merge_gbs, "frac_hbm": merge_gbs / PEAK_HBM_GBS,
-                      "bytes": mbytes, "bytes_live_rows": mbytes_live,
-                      "gbs_live_rows": mbytes_live / (t_merge * 1e-3) / 1e9,
-                      "traffic": measured_traffic("lse_merge_kernel", a.workload)},
-        "roofline": {"bound": "mfma", "achieved": tile_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": tile_tflops / peak, "traffic": measured_traffic(tile_kernel, a.workload),
+        "config": head["config"],
+        "tile_fwd": tf,
+        "lse_merge": head["lse_merge"],
+        "roofline": {"bound": "mfma", "achieved": tf["tflops"], "peak": tf["peak"],
+                     "unit": "TFLOP/s", "frac": tf["frac_peak"], "traffic": tf["traffic"],
                      "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE)",
-                     "kernel": tile_kernel},
+                     "kernel": tf["kernel"]},
+        "block_list": head["block_list"],
     }
-    # Row a1 (host): the block list of this tile, library call against the oracle's brute force.
-    t0 = time.perf_counter()
-    for _ in range(1000):
-        mat.block_list(R, C, r, c, w.causal, w.kv_rotate)
-    bl_us = (time.perf_counter() - t0) * 1e3
-    result["block_list"] = {"us": bl_us, "blocks": len(blocks),
-                            "note": "host call through the Python binding, mean of 1000"}
-    if not a.no_cpu_baseline:
-        import oracle
-        t0 = time.perf_counter()
-        for _ in range(20):
-            ref_bl = oracle.block_list_ref(R, C, r, c, w.causal, w.kv_rotate)
-        result["block_list"]["oracle_us"] = (time.perf_counter() - t0) / 20 * 1e6
-        result["block_list"]["equal_to_oracle"] = ref_bl == blocks
+    for key in ("tile_bwd", "cpu_baseline"):
+        if key in head:
+            result[key] = head[key]
     props = torch.cuda.get_device_properties(dev)
     result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                         "compute_units": props.multi_processor_count,
                         "memory_gib": round(props.total_memory / 2 ** 30, 1)}
-    if a.backward_steps > 0 and w.dtype == "bf16":
-        result["tile_bwd"] = backward_leg(a.backward_steps, a.workload, w, q, k, v, o_own, l_own,
-                                          q_parts, blocks, flops, dev)
-    if a.copy_calibration > 0:
-        src = torch.empty(a.copy_calibration << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] copy calibration: {a.copy_calibration} MiB read + written by one copy kernel")
-    if not a.no_cpu_baseline:
-        log("[bench] timing the oracle on host cores")
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, q_parts, kv_parts, flops, o_parts,
-                                              l_parts, a.cpu_budget)
+    others = _others(a.others)
+    if others:
+        per = {}
+        for wid in others:
+            if wid == a.workload:
+                per[str(wid)] = {k_: v_ for k_, v_ in head.items()}
+                continue
+            res, _ = measure_workload(wid, a.others_steps, 1, 2 if a.backward_steps > 0 else 0,
+                                      0.0 if a.no_cpu_baseline else a.others_cpu_budget, 0, dev)
+            per[str(wid)] = res
+        result["per_workload"] = per
     print(json.dumps(result), flush=True)
 
 

@@ -24,7 +24,11 @@
  *
  * Conventions
  *   - All integers are int32_t unless stated.  Tensors are dense, row-major,
- *     token-major, and every device pointer must be 16-byte aligned.
+ *     token-major.  Device pointers to bf16/f32 row data (q, k, v, o, dout,
+ *     partial and merged outputs, gradients) must be 16-byte aligned; the
+ *     per-row float32 arrays (lse, lse_parts, lse_out, delta) 4-byte aligned,
+ *     so that a tile's lse may be written straight into one slot of a
+ *     merge's [n, rows] lse array whatever rows is.
  *   - Device buffers and the stream belong to the caller.  The library
  *     allocates no device memory and keeps no state between calls except a
  *     thread-local text of the last error (mesh_attn_last_error).

@@ -20,6 +20,7 @@ namespace {
 thread_local std::string g_last_error;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 int hip_status(hipError_t e, const char* what) {
     if (e == hipSuccess) {
@@ -240,8 +241,9 @@ extern "C" int mesh_attn_tile_fwd(const mesh_attn_tile_desc* desc, const void* q
     const mesh_attn_tile_desc& d = *desc;
     if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr)
         return failw(MESH_ATTN_ERR_INVALID, who, "NULL tensor pointer");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return failw(MESH_ATTN_ERR_INVALID, who, "tensor pointer not 16-byte aligned");
+    if (!aligned4(lse)) return failw(MESH_ATTN_ERR_INVALID, who, "lse pointer not 4-byte aligned");
     TileParams p;
     const int st = plan_tile_fwd(who, d, p);
     if (st != MESH_ATTN_OK) return st;
@@ -336,9 +338,11 @@ extern "C" int mesh_attn_tile_bwd(const mesh_attn_tile_desc* desc, const void* q
     if (q == nullptr || k == nullptr || v == nullptr || dout == nullptr || lse == nullptr ||
         delta == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
         return failw(MESH_ATTN_ERR_INVALID, who, "NULL tensor pointer");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(lse) ||
-        !aligned16(delta) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv))
         return failw(MESH_ATTN_ERR_INVALID, who, "tensor pointer not 16-byte aligned");
+    if (!aligned4(lse) || !aligned4(delta))
+        return failw(MESH_ATTN_ERR_INVALID, who, "lse or delta pointer not 4-byte aligned");
     BwdDqParams pq;
     BwdDkvParams pk;
     const int st = plan_tile_bwd(who, d, pq, pk);

@@ -337,10 +337,61 @@ def check_block_list_kinds(block_list, R, C):
         assert order == sorted(order) and len(order) == len(set(order)), "not kv-slot major"
         nc = block_list(R, C, r, c, False, True)
         assert all(b[4] == FULL for b in nc), "non-causal tile must be all FULL"
+
+
+def check_block_list_contiguous(block_list, R, C):
+    """Contiguous (un-rotated) tiles: plain 2-D block tiling of the Q-KV
+    matrix, checked by properties rather than by the index formula.
+
+    * Every tile's Q set is the C partitions of its own mesh row, in order
+      (a GPU receives Q only from its mesh-row peers; tutorial page, "From
+      1-D ring to 2-D mesh", panel (b)).
+    * Every tile's KV set is a run of R consecutive partitions in increasing
+      order ("contiguous" taken literally: no stride, no rotation).
+    * The tiles of the mesh cover each (Q partition, KV partition) block of
+      the P x P matrix exactly once.
+    * Tiles of one mesh row take their runs left to right: column c's run
+      lies before column c+1's.
+    * Causal classes follow the partition order, and a contiguous tile may
+      hold more than one diagonal block (e.g. 2x2 tile (0,0)).
+    """
+    P = R * C
+    seen = {}
     for r, c in itertools.product(range(R), range(C)):
-        _, qset, kvset = _tile_sets(block_list, R, C, r, c, False, False)
-        assert qset == [r * C + t for t in range(C)], "contiguous Q set"
-        assert kvset == [c * R + k for k in range(R)], "contiguous KV set"
+        bl, qset, kvset = _tile_sets(block_list, R, C, r, c, False, False)
+        assert len(bl) == R * C, "tile must hold C*R blocks"
+        assert sorted(qset) == qset and all(p // C == r for p in qset) and len(set(qset)) == C, \
+            "contiguous Q set is not the mesh row"
+        assert len(kvset) == R and all(b - a == 1 for a, b in zip(kvset, kvset[1:])), \
+            "contiguous KV set is not a run of consecutive partitions"
+        assert 0 <= kvset[0] and kvset[-1] < P, "KV partition outside the sequence"
+        for _, _, qp, kp, _ in bl:
+            seen[(qp, kp)] = seen.get((qp, kp), 0) + 1
+        if c + 1 < C:
+            _, _, right = _tile_sets(block_list, R, C, r, c + 1, False, False)
+            assert kvset[-1] < right[0], "column runs not ordered left to right"
+        cbl = block_list(R, C, r, c, True, False)
+        for q_slot, kv_slot, qp, kp, kind in cbl:
+            want = FULL if kp < qp else (DIAG if kp == qp else SKIP)
+            assert kind == want, "contiguous causal kind disagrees with partition order"
+    assert len(seen) == P * P and set(seen.values()) == {1}, \
+        "contiguous tiles do not partition the matrix"
+
+
+def check_block_list_fp32_workload_tile(block_list):
+    """The literal geometry the fp32 workload statement gives: a 2x2 mesh
+    with contiguous KV partitions, whose tile (0,0) holds Q partitions {0,1}
+    against KV partitions {0,1}, merged with the partial of the tile that
+    holds KV partitions {2,3} (its mesh-row sibling (0,1))."""
+    bl, qset, kvset = _tile_sets(block_list, 2, 2, 0, 0, False, False)
+    assert qset == [0, 1] and kvset == [0, 1], "fp32 workload tile (0,0)"
+    assert sorted((b[2], b[3]) for b in bl) == [(0, 0), (0, 1), (1, 0), (1, 1)]
+    assert all(b[4] == FULL for b in bl), "non-causal tile must be all FULL"
+    _, qset1, kvset1 = _tile_sets(block_list, 2, 2, 0, 1, False, False)
+    assert qset1 == [0, 1] and kvset1 == [2, 3], "fp32 workload sibling tile (0,1)"
+    # Causal 2x2 tile (0,0) holds both diagonal blocks of its Q partitions.
+    kinds = {(b[2], b[3]): b[4] for b in block_list(2, 2, 0, 0, True, False)}
+    assert kinds == {(0, 0): DIAG, (0, 1): SKIP, (1, 0): FULL, (1, 1): DIAG}
 
 
 # --------------------------------------------------------------------------- backward

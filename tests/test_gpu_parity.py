@@ -187,3 +187,31 @@ def test_per_kv_slot_subtiles_merge_to_single_launch():
     fin = np.isfinite(want_l)
     assert np.max(np.abs(got_o - want_o)) <= 2e-2
     assert np.max(np.abs(got_l[fin] - want_l[fin])) <= 1e-3
+
+
+@pytest.mark.parametrize("R,C,r,c,L,hq,hkv", [(8, 2, 4, 1, 48, 4, 2), (16, 2, 8, 1, 40, 4, 2),
+                                             (16, 1, 5, 0, 33, 8, 1)])
+def test_running_pairwise_merge_one_kv_slot_at_a_time(R, C, r, c, L, hq, hkv):
+    """A tile computed one KV slot at a time, in rotation order, each partial
+    folded into a running result by a two-way merge whose bf16 output is the
+    next step's input (n-1 bf16 roundings of O), equals the oracle over the
+    whole tile within the bf16 bounds.  8 and 16 KV slots."""
+    import torch
+    import long_context_distributed_amd as mat
+    w = workloads.small("bf16", L, R, C, r, c, True, True, hq, hkv, 128)
+    say(f"[case] running merge {w.name}")
+    t = run_tile(w)
+    rows = t["q"].shape[0] * hq
+    o_run = lse_run = None
+    for j in range(R):
+        step_blocks = [b for b in t["blocks"] if b[1] == j]
+        o_j, lse_j = mat.tile_fwd(t["q"], t["k"], t["v"], step_blocks, L)
+        if o_run is None:
+            o_run, lse_run = o_j, lse_j
+            continue
+        o_m, lse_m = mat.lse_merge(torch.stack([o_run.view(rows, 128), o_j.view(rows, 128)]),
+                                   torch.stack([lse_run.view(rows), lse_j.view(rows)]))
+        o_run, lse_run = o_m.view_as(o_j), lse_m.view_as(lse_j)
+    ref_o, ref_lse = oracle.tile_rows_ref(t["q"], t["k"], t["v"], t["q_parts"], t["kv_parts"],
+                                          L, True, 1.0 / math.sqrt(128))
+    compare(o_run, lse_run, ref_o, ref_lse, "bf16", what=f"running merge over {R} KV slots")

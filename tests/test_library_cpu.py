@@ -63,6 +63,21 @@ def test_block_list_bit_exact_larger_meshes(lib, R, C):
                 oracle.block_list_ref(R, C, r, c, causal, rot)
 
 
+def test_block_list_pins_hold_for_the_library(lib):
+    """The library's own lists satisfy the oracle's property pins directly
+    (rotated geometry, causal counts, contiguous tiling, the fp32 workload's
+    literal tile), not only equality with the oracle."""
+    from tests import oracle_pins as pins
+
+    def bl(R, C, r, c, causal, rot):
+        return _lib_block_list(lib, R, C, r, c, int(causal), int(rot))
+    for R, C in [(2, 2), (4, 4), (3, 5), (8, 8), (16, 4)]:
+        pins.check_block_list_geometry(bl, R, C)
+        pins.check_block_list_kinds(bl, R, C)
+        pins.check_block_list_contiguous(bl, R, C)
+    pins.check_block_list_fp32_workload_tile(bl)
+
+
 def test_block_list_errors(lib):
     n = ctypes.c_int32(0)
     arr = (_lib.Block * 4)()
@@ -129,7 +144,25 @@ def test_tile_null_and_misaligned(lib):
     assert _tile(lib, d, by_ref=False) == _lib.ERR_INVALID
     for field in ("q", "k", "v", "o", "lse"):
         assert _tile(lib, d, **{field: None}) == _lib.ERR_INVALID
+    for field in ("q", "k", "v", "o"):
         assert _tile(lib, d, **{field: FAKE + 4}) == _lib.ERR_INVALID
+        assert b"16-byte" in lib.mesh_attn_last_error()
+    assert _tile(lib, d, lse=FAKE + 2) == _lib.ERR_INVALID
+    assert b"4-byte" in lib.mesh_attn_last_error()
+
+
+def test_tile_lse_needs_only_four_byte_alignment(lib):
+    """A tile's lse may start at any float of a merge's [n, rows] lse array.
+    The block list here is invalid, so the call fails validation after the
+    pointer checks and nothing is launched: the error is the block's, not
+    the pointer's."""
+    bad = [(0, 0, 0, 0, 0), (0, 0, 0, 0, 0)]  # duplicated block
+    for off in (4, 8, 12):
+        assert _tile(lib, _desc(blocks=bad), lse=FAKE + off) == _lib.ERR_INVALID
+        assert b"duplicated" in lib.mesh_attn_last_error()
+        assert _bwd(lib, _desc(blocks=bad), lse=FAKE + off, delta=FAKE + 16 + off) == \
+            _lib.ERR_INVALID
+        assert b"duplicated" in lib.mesh_attn_last_error()
 
 
 def test_tile_unsupported(lib):
@@ -220,7 +253,11 @@ def test_tile_bwd_null_misaligned_unsupported(lib):
     assert _bwd(lib, d, by_ref=False) == _lib.ERR_INVALID
     for field in ("q", "k", "v", "dout", "lse", "delta", "dq", "dk", "dv"):
         assert _bwd(lib, d, **{field: None}) == _lib.ERR_INVALID
+    for field in ("q", "k", "v", "dout", "dq", "dk", "dv"):
         assert _bwd(lib, d, **{field: FAKE + 4}) == _lib.ERR_INVALID
+    for field in ("lse", "delta"):
+        assert _bwd(lib, d, **{field: FAKE + 2}) == _lib.ERR_INVALID
+        assert b"4-byte" in lib.mesh_attn_last_error()
     assert _bwd(lib, _desc(head_dim=64)) == _lib.ERR_UNSUPPORTED
     assert _bwd(lib, _desc(dtype=_lib.F32)) == _lib.ERR_UNSUPPORTED
 

@@ -19,6 +19,15 @@ def test_kinds(R, C):
     pins.check_block_list_kinds(block_list, R, C)
 
 
+@pytest.mark.parametrize("R,C", [(1, 1), (2, 2), (4, 4), (8, 8), (16, 4), (3, 5), (1, 6), (6, 1)])
+def test_contiguous_tiling(R, C):
+    pins.check_block_list_contiguous(block_list, R, C)
+
+
+def test_fp32_workload_tile_literal():
+    pins.check_block_list_fp32_workload_tile(block_list)
+
+
 @pytest.mark.parametrize("L", [2, 3, 5])
 def test_classification_independent_of_length(L):
     for r in range(4):

@@ -98,12 +98,38 @@ def _bl_q_from_column(R, C, r, c, causal, rot):
     return out
 
 
+def _bl_contiguous_strided(R, C, r, c, causal, rot):
+    """Contiguous mode read as a column stride: KV partitions c + k*C."""
+    if rot:
+        return oracle.block_list_ref(R, C, r, c, causal, rot)
+    out = []
+    for (qs, ks, qp, kp, kind) in oracle.block_list_ref(R, C, r, c, causal, rot):
+        kp = c + ks * C
+        kind = oracle.FULL if not causal else (0 if kp < qp else (1 if kp == qp else 2))
+        out.append((qs, ks, qp, kp, kind))
+    return out
+
+
+def _bl_contiguous_columns_reversed(R, C, r, c, causal, rot):
+    """Contiguous runs handed to the mesh columns right to left."""
+    if rot:
+        return oracle.block_list_ref(R, C, r, c, causal, rot)
+    out = []
+    for (qs, ks, qp, kp, kind) in oracle.block_list_ref(R, C, r, c, causal, rot):
+        kp = (C - 1 - c) * R + ks
+        kind = oracle.FULL if not causal else (0 if kp < qp else (1 if kp == qp else 2))
+        out.append((qs, ks, qp, kp, kind))
+    return out
+
+
 BLOCK_MUTANTS = {
     "rotation along the row-major index": _bl_rot_row_major,
     "kinds flipped": _bl_kind_flipped,
     "q-slot major order": _bl_q_major,
     "rotated and contiguous swapped": _bl_modes_swapped,
     "Q set taken from the column": _bl_q_from_column,
+    "contiguous KV strided by the column count": _bl_contiguous_strided,
+    "contiguous KV runs in reversed column order": _bl_contiguous_columns_reversed,
 }
 
 
@@ -165,6 +191,8 @@ def _block_checks(bl):
     for R, C in [(4, 4), (3, 5), (2, 3)]:
         yield lambda R=R, C=C: pins.check_block_list_geometry(bl, R, C)
         yield lambda R=R, C=C: pins.check_block_list_kinds(bl, R, C)
+        yield lambda R=R, C=C: pins.check_block_list_contiguous(bl, R, C)
+    yield lambda: pins.check_block_list_fp32_workload_tile(bl)
 
 
 def _bwd_checks(bw):

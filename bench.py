@@ -412,6 +412,7 @@ def measure_workload(wid, steps, warmup, backward_steps, cpu_budget, copy_calibr
             ref_bl = oracle.block_list_ref(R, C, r, c, w.causal, w.kv_rotate)
         res["block_list"]["oracle_us"] = (time.perf_counter() - t0) / 20 * 1e6
         res["block_list"]["equal_to_oracle"] = ref_bl == blocks
+    res["plan"] = plan_leg(w, blocks, t_tile)
     if backward_steps > 0 and w.dtype == "bf16":
         res["tile_bwd"] = backward_leg(backward_steps, wid, w, q, k, v, o_own, l_own,
                                        q_parts, blocks, flops, dev)
@@ -429,6 +430,53 @@ def measure_workload(wid, steps, warmup, backward_steps, cpu_budget, copy_calibr
     del q, k, v, o_parts, l_parts, o_own, l_own, o_m, l_m
     torch.cuda.empty_cache()
     return res, ms_step
+
+
+XGMI_LINK_GBS = 153.0   # one MI355X xGMI link, GB/s per direction (AMD spec figure)
+
+
+def plan_costs(w, blocks, t_tile_ms, link_gbs=XGMI_LINK_GBS):
+    """Costs of the planner's step model for one tile: transfer times of a Q
+    partition, a KV partition and a partial output over one link, and the
+    time of a FULL and a DIAG block from the measured tile time shared over
+    the visible pairs."""
+    elt = 2 if w.dtype == "bf16" else 4
+    L, d = w.part_len, w.head_dim
+    pairs = sum(L * L if b[4] == 0 else L * (L + 1) // 2 if b[4] == 1 else 0 for b in blocks)
+    per_pair = t_tile_ms * 1e-3 / pairs
+    bw = link_gbs * 1e9
+    return {"recv_q_s": L * w.heads_q * d * elt / bw,
+            "recv_kv_s": 2 * L * w.heads_kv * d * elt / bw,
+            "send_o_s": L * w.heads_q * (d * elt + 4) / bw,
+            "full_block_s": per_pair * L * L,
+            "diag_block_s": per_pair * (L * (L + 1) // 2)}
+
+
+def plan_leg(w, blocks, t_tile_ms):
+    """Row f2 (host): the greedy plan of this GPU's tile with the measured
+    block time and one xGMI link, beside the eager variant and the lower
+    bound max(total transfer, total compute)."""
+    import long_context_distributed_amd as mat
+    costs = plan_costs(w, blocks, t_tile_ms)
+    R, C, r, c = w.mesh_rows, w.mesh_cols, w.tile_row, w.tile_col
+    t0 = time.perf_counter()
+    for _ in range(100):
+        steps = mat.plan(R, C, r, c, w.causal, w.kv_rotate, costs)
+    plan_us = (time.perf_counter() - t0) * 1e4
+    eager = mat.plan(R, C, r, c, w.causal, w.kv_rotate, costs, delay=False)
+    comm = sum(st["comm_s"] for st in steps)
+    comp = sum(st["compute_s"] for st in steps)
+    span = steps[-1]["end_s"] if steps else 0.0
+    res = {"link_gbs": XGMI_LINK_GBS, "costs_s": costs, "steps": len(steps),
+           "makespan_ms": span * 1e3, "eager_makespan_ms": (eager[-1]["end_s"] if eager else 0.0) * 1e3,
+           "transfer_ms": comm * 1e3, "compute_ms": comp * 1e3,
+           "lower_bound_ms": max(comm, comp) * 1e3,
+           "compute_busy": comp / span if span else 1.0, "plan_us": plan_us,
+           "note": "host planner (step model), not a multi-GPU run"}
+    log(f"[bench] plan: {len(steps)} steps, makespan {span * 1e3:.2f} ms (eager "
+        f"{res['eager_makespan_ms']:.2f} ms, bound {res['lower_bound_ms']:.2f} ms), "
+        f"compute busy {100 * res['compute_busy']:.1f}%, planner {plan_us:.0f} us")
+    return res
 
 
 def _others(spec):
@@ -492,7 +540,7 @@ def main():
                      "kernel": tf["kernel"]},
         "block_list": head["block_list"],
     }
-    for key in ("tile_bwd", "cpu_baseline"):
+    for key in ("plan", "tile_bwd", "cpu_baseline"):
         if key in head:
             result[key] = head[key]
     props = torch.cuda.get_device_properties(dev)

@@ -214,6 +214,84 @@ MESH_ATTN_API int mesh_attn_tile_bwd(const mesh_attn_tile_desc *desc, const void
                        const void *v, const void *dout, const float *lse, const float *delta,
                        float *dq, float *dk, float *dv, void *hip_stream);
 
+/* Transfers of a plan step (mesh_attn_plan). */
+enum {
+    MESH_ATTN_COMM_NONE = 0,    /* no transfer in this step */
+    MESH_ATTN_COMM_RECV_Q = 1,  /* receive the Q partition of Q slot `slot` */
+    MESH_ATTN_COMM_RECV_KV = 2, /* receive the K and V partition of KV slot `slot` */
+    MESH_ATTN_COMM_SEND_O = 3   /* send the partial output (O, lse) of Q slot `slot` to its owner */
+};
+
+/* Costs of the plan's step model, in seconds (finite, >= 0).  A caller
+ * derives them from its shapes: a Q partition is L*H_q*d*s bytes, a KV
+ * partition 2*L*H_kv*d*s, a partial output L*H_q*(d*s + 4) (s = bytes per
+ * element), each over the link's bandwidth; a FULL block is 4*L*L*d*H_q
+ * flops and a DIAG block 4*L*(L+1)/2*d*H_q, each over the tile kernel's
+ * measured rate. */
+typedef struct {
+    double recv_q_s;      /* receive one Q partition */
+    double recv_kv_s;     /* receive one KV partition (K and V) */
+    double send_o_s;      /* send one partial output */
+    double full_block_s;  /* compute one FULL block */
+    double diag_block_s;  /* compute one DIAG block */
+    int32_t delay;        /* 1: hold ready blocks back to fill later transfers (the
+                           * greedy rule); 0: compute every ready block at once */
+} mesh_attn_plan_costs;
+
+/* One step of a plan: a transfer beside a run of blocks of `order`. */
+typedef struct {
+    int32_t comm;         /* MESH_ATTN_COMM_* */
+    int32_t slot;         /* Q slot (RECV_Q, SEND_O) or KV slot (RECV_KV); -1 for NONE */
+    int32_t block_begin;  /* the step computes order[block_begin .. block_begin+block_count) */
+    int32_t block_count;
+    double comm_s;        /* the transfer's time */
+    double compute_s;     /* the blocks' time */
+    double start_s;       /* simulated start: the previous step's end (0 for the first) */
+    double end_s;         /* start_s + max(comm_s, compute_s) */
+} mesh_attn_plan_step;
+
+/*
+ * mesh_attn_plan - the greedy communication/computation schedule of GPU
+ * (row, col) of a mesh_rows x mesh_cols mesh (tutorial page, section
+ * "Greedy algorithm"; greedy scheduling in the abstract on the mlsanity
+ * page).  Pure host code: needs no GPU.
+ *
+ * The tile is mesh_attn_block_list(mesh_rows, mesh_cols, row, col, causal,
+ * kv_rotate).  The GPU holds partition row*mesh_cols + col from the start;
+ * a non-SKIP block can be computed once its Q slot's and KV slot's
+ * partitions are present.  Transfers: receive each Q or KV partition some
+ * non-SKIP block needs and the GPU does not hold, and send back the partial
+ * output of each Q slot that belongs to another GPU once that row's
+ * non-SKIP blocks are computed.  Steps run in lock-step: each runs at most
+ * one transfer beside a set of ready blocks and lasts max(transfer,
+ * compute); data received in a step is usable from the next step.
+ *   Transfer choice: the pending receive that makes the most blocks
+ *     computable; ties to the one whose slot has more non-SKIP blocks, then
+ *     Q before KV, then the lower slot.  Sends follow the receives (one goes
+ *     earlier only if no pending receive unlocks anything), ready sends in
+ *     slot order.
+ *   Compute choice (delay = 1): ready blocks in priority order until their
+ *     time covers the step's transfer; the rest wait.  Priority: rows whose
+ *     partial is sent first, rows with fewer blocks left first, then Q slot,
+ *     then KV slot.  A step with no transfer possible finishes the next row
+ *     to be sent (or, with no send left, computes everything that remains).
+ *     delay = 0 computes every ready block at once.
+ *
+ * Outputs: steps[0 .. *n_steps) and order[0 .. *n_order), the non-SKIP
+ * blocks in compute order (block-list tuples).  The makespan is
+ * steps[*n_steps - 1].end_s (0 steps for a tile with no work and no
+ * transfer).  If steps or order is NULL or a capacity is too small, the two
+ * counts are written and MESH_ATTN_ERR_CAPACITY is returned (nothing else is
+ * written): a size query.  MESH_ATTN_ERR_INVALID: NULL costs, n_steps or
+ * n_order; a cost not finite or negative; delay not 0 or 1; mesh_rows > 64
+ * or mesh_cols > 64 (the tile limits); anything mesh_attn_block_list
+ * rejects.
+ */
+MESH_ATTN_API int mesh_attn_plan(int32_t mesh_rows, int32_t mesh_cols, int32_t row, int32_t col,
+                   int32_t causal, int32_t kv_rotate, const mesh_attn_plan_costs *costs,
+                   mesh_attn_plan_step *steps, int32_t step_capacity, int32_t *n_steps,
+                   mesh_attn_block *order, int32_t order_capacity, int32_t *n_order);
+
 /* Text of a status code (static storage). */
 MESH_ATTN_API const char *mesh_attn_status_string(int status);
 

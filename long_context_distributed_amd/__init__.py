@@ -9,15 +9,18 @@ every step of the computation runs in the library's HIP kernels.
     lse_merge(o_parts, lse_parts) -> (o, lse)
     bwd_delta(o, dout) -> delta
     tile_bwd(q, k, v, dout, lse, delta, blocks, part_len, softmax_scale=None) -> (dq, dk, dv)
+    plan(mesh_rows, mesh_cols, row, col, causal, kv_rotate, costs, delay=True) -> [steps]
 """
 import ctypes
 import math
 
 from . import _lib
-from ._lib import BF16, DIAG, F32, FULL, SKIP  # noqa: F401
+from ._lib import (BF16, COMM_NONE, COMM_RECV_KV, COMM_RECV_Q, COMM_SEND_O, DIAG, F32,  # noqa: F401
+                   FULL, SKIP)
 
-__all__ = ["MeshAttnError", "block_list", "tile_fwd", "lse_merge", "bwd_delta", "tile_bwd",
-           "FULL", "DIAG", "SKIP", "library_path"]
+__all__ = ["MeshAttnError", "block_list", "tile_fwd", "lse_merge", "bwd_delta", "tile_bwd", "plan",
+           "FULL", "DIAG", "SKIP", "COMM_NONE", "COMM_RECV_Q", "COMM_RECV_KV", "COMM_SEND_O",
+           "library_path"]
 
 
 class MeshAttnError(RuntimeError):
@@ -234,3 +237,32 @@ def tile_bwd(q, k, v, dout, lse, delta, blocks, part_len, softmax_scale=None, dq
                                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                        _stream_handle(stream, q.device)))
     return dq, dk, dv
+
+
+def plan(mesh_rows, mesh_cols, row, col, causal, kv_rotate, costs, delay=True):
+    """Greedy communication/computation schedule of GPU (row, col).
+
+    costs: mapping with recv_q_s, recv_kv_s, send_o_s, full_block_s and
+    diag_block_s (seconds).  Returns a list of steps, each a dict: comm
+    (COMM_NONE / COMM_RECV_Q / COMM_RECV_KV / COMM_SEND_O), slot (-1 for
+    none), blocks (block tuples computed in the step, in order), comm_s,
+    compute_s, start_s, end_s.  Host code; needs no GPU.
+    """
+    lib = _lib.load()
+    c = _lib.PlanCosts(float(costs["recv_q_s"]), float(costs["recv_kv_s"]),
+                       float(costs["send_o_s"]), float(costs["full_block_s"]),
+                       float(costs["diag_block_s"]), int(bool(delay)))
+    ns, no = ctypes.c_int32(0), ctypes.c_int32(0)
+    args = (mesh_rows, mesh_cols, row, col, int(bool(causal)), int(bool(kv_rotate)), ctypes.byref(c))
+    st = lib.mesh_attn_plan(*args, None, 0, ctypes.byref(ns), None, 0, ctypes.byref(no))
+    if st != _lib.ERR_CAPACITY:
+        _check(lib, st)
+    steps = (_lib.PlanStep * max(1, ns.value))()
+    order = (_lib.Block * max(1, no.value))()
+    _check(lib, lib.mesh_attn_plan(*args, steps, ns.value, ctypes.byref(ns), order, no.value,
+                                   ctypes.byref(no)))
+    blocks = [(b.q_slot, b.kv_slot, b.q_part, b.kv_part, b.kind) for b in order[:no.value]]
+    return [{"comm": s.comm, "slot": s.slot,
+             "blocks": blocks[s.block_begin:s.block_begin + s.block_count],
+             "comm_s": s.comm_s, "compute_s": s.compute_s, "start_s": s.start_s, "end_s": s.end_s}
+            for s in steps[:ns.value]]

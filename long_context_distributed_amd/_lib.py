@@ -22,6 +22,11 @@ FULL = 0
 DIAG = 1
 SKIP = 2
 
+COMM_NONE = 0
+COMM_RECV_Q = 1
+COMM_RECV_KV = 2
+COMM_SEND_O = 3
+
 MAX_Q_SLOTS = 64
 MAX_KV_SLOTS = 64
 MAX_BLOCKS = 1024
@@ -29,7 +34,7 @@ MAX_HEADS = 4096
 
 # Every symbol include/mesh_attn.h declares.
 EXPORTS = ("mesh_attn_block_list", "mesh_attn_tile_fwd", "mesh_attn_lse_merge",
-           "mesh_attn_bwd_delta", "mesh_attn_tile_bwd",
+           "mesh_attn_bwd_delta", "mesh_attn_tile_bwd", "mesh_attn_plan",
            "mesh_attn_status_string", "mesh_attn_last_error", "mesh_attn_version")
 
 
@@ -45,6 +50,19 @@ class TileDesc(ctypes.Structure):
                 ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("blocks", ctypes.POINTER(Block)), ("n_blocks", ctypes.c_int32)]
+
+
+class PlanCosts(ctypes.Structure):
+    _fields_ = [("recv_q_s", ctypes.c_double), ("recv_kv_s", ctypes.c_double),
+                ("send_o_s", ctypes.c_double), ("full_block_s", ctypes.c_double),
+                ("diag_block_s", ctypes.c_double), ("delay", ctypes.c_int32)]
+
+
+class PlanStep(ctypes.Structure):
+    _fields_ = [("comm", ctypes.c_int32), ("slot", ctypes.c_int32),
+                ("block_begin", ctypes.c_int32), ("block_count", ctypes.c_int32),
+                ("comm_s", ctypes.c_double), ("compute_s", ctypes.c_double),
+                ("start_s", ctypes.c_double), ("end_s", ctypes.c_double)]
 
 
 _LIB = None
@@ -73,6 +91,10 @@ def load():
     lib.mesh_attn_bwd_delta.restype = ctypes.c_int
     lib.mesh_attn_tile_bwd.argtypes = [ctypes.POINTER(TileDesc)] + [vp] * 10
     lib.mesh_attn_tile_bwd.restype = ctypes.c_int
+    lib.mesh_attn_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(PlanCosts),
+                                   ctypes.POINTER(PlanStep), i32, ctypes.POINTER(i32),
+                                   ctypes.POINTER(Block), i32, ctypes.POINTER(i32)]
+    lib.mesh_attn_plan.restype = ctypes.c_int
     lib.mesh_attn_status_string.argtypes = [ctypes.c_int]
     lib.mesh_attn_status_string.restype = ctypes.c_char_p
     lib.mesh_attn_last_error.argtypes = []

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmeshattn.so")
 
-SOURCES = ["api.cpp", "block_list.cpp", "tile_fwd_bf16.hip", "tile_fwd_f32.hip", "lse_merge.hip",
+SOURCES = ["api.cpp", "block_list.cpp", "plan.cpp", "tile_fwd_bf16.hip", "tile_fwd_f32.hip", "lse_merge.hip",
            "tile_bwd_bf16.hip", "bwd_delta.hip"]
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden", "-I", INCLUDE, "-I", CSRC,

@@ -15,6 +15,9 @@ with no blocking, no online softmax and no fusion:
   natural-log log-sum-exp of the scaled scores.
 * ``lse_merge_ref``  - the log-sum-exp weighted combination of partial
   (output, lse) pairs.
+* ``greedy_plan_ref`` / ``optimal_makespan_ref`` - the greedy schedule of
+  transfers and block computations of one mesh GPU, and the exhaustive
+  optimum of the same step model on tiny meshes.
 * ``attention_bwd_ref`` / ``tile_bwd_ref`` / ``bwd_delta_ref`` - the gradients
   of attention (dQ, dK, dV) split into the share of one tile's visible pairs,
   given the rows' final lse and D = rowsum(dO * O).
@@ -28,6 +31,7 @@ from .block_list import FULL, DIAG, SKIP, block_list_ref, mesh_tile_sets_ref
 from .attention import attention_ref, tile_rows_ref, tile_positions_ref
 from .merge import lse_merge_ref
 from .backward import attention_bwd_ref, bwd_delta_ref, full_grads_ref, tile_bwd_ref
+from .schedule import greedy_plan_ref, optimal_makespan_ref, plan_makespan_ref
 
 __all__ = [
     "FULL", "DIAG", "SKIP",
@@ -35,4 +39,5 @@ __all__ = [
     "attention_ref", "tile_rows_ref", "tile_positions_ref",
     "lse_merge_ref",
     "attention_bwd_ref", "bwd_delta_ref", "full_grads_ref", "tile_bwd_ref",
+    "greedy_plan_ref", "optimal_makespan_ref", "plan_makespan_ref",
 ]

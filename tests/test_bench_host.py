@@ -116,3 +116,19 @@ def test_profile_summaries_are_well_formed():
         assert cmds and all(" -- python bench.py " in c and "--no-cpu-baseline" in c and
                             "--copy-calibration 1024" in c for c in cmds), path
         assert "_work" not in text, path
+
+
+def test_plan_costs_of_the_1m_token_tile():
+    """Transfer sizes of the 8x8 mesh tile (L=16384, GQA 32/8, d=128, bf16):
+    a Q partition 128 MiB, a KV partition 64 MiB, a partial output 130 MiB
+    (with its lse); block times share the tile time over visible pairs."""
+    w = workloads.WORKLOADS[4]
+    blocks = oracle.block_list_ref(8, 8, 4, 4, True, True)
+    c = bench.plan_costs(w, blocks, 100.0, link_gbs=100.0)
+    assert c["recv_q_s"] == 16384 * 32 * 128 * 2 / 100e9
+    assert c["recv_kv_s"] == 2 * 16384 * 8 * 128 * 2 / 100e9
+    assert c["send_o_s"] == 16384 * 32 * (128 * 2 + 4) / 100e9
+    assert math.isclose(35 * c["full_block_s"] + c["diag_block_s"], 0.1, rel_tol=1e-12)
+    res = bench.plan_leg(w, blocks, 100.0)
+    assert res["lower_bound_ms"] <= res["makespan_ms"] <= res["eager_makespan_ms"] + 1e-9
+    assert math.isclose(res["compute_ms"], 100.0, rel_tol=1e-9)

@@ -81,6 +81,19 @@ DRIVER = textwrap.dedent("""
     assert lib.mesh_attn_lse_merge(0, 16, 128, 0, FAKE, FAKE, FAKE, FAKE, None) == _lib.ERR_INVALID
     assert lib.mesh_attn_bwd_delta(1 << 20, 128, 0, FAKE, FAKE, FAKE, None) == _lib.ERR_HIP
     assert lib.mesh_attn_bwd_delta(16, 12, 0, FAKE, FAKE, FAKE, None) == _lib.ERR_INVALID
+    # the greedy planner: equal to the oracle's plans, size queries, invalid costs
+    import long_context_distributed_amd as mat
+    costs = dict(recv_q_s=1.0, recv_kv_s=0.5, send_o_s=1.25, full_block_s=0.75, diag_block_s=0.375)
+    for R, C in [(1, 1), (2, 2), (3, 5), (8, 8), (16, 4), (64, 1)]:
+        for r, c in sorted(set([(0, 0), (R // 2, C // 2), (R - 1, C - 1)])):
+            for causal, rot, delay in itertools.product((0, 1), repeat=3):
+                got = mat.plan(R, C, r, c, causal, rot, costs, delay)
+                want = oracle.greedy_plan_ref(R, C, r, c, causal, rot, costs, bool(delay))
+                assert [(x["comm"], x["slot"], x["blocks"], x["end_s"]) for x in got] == \
+                    [(x["comm"], x["slot"], x["blocks"], x["end_s"]) for x in want]
+    pc = _lib.PlanCosts(1.0, 1.0, 1.0, -1.0, 1.0, 1)
+    assert lib.mesh_attn_plan(2, 2, 0, 0, 1, 1, ctypes.byref(pc), None, 0, ctypes.byref(n), None, 0,
+                              ctypes.byref(n)) == _lib.ERR_INVALID
     print("sanitized host path ok")
 """)
 
@@ -103,8 +116,8 @@ def test_host_code_under_asan_and_ubsan(tmp_path):
     cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fsanitize=address,undefined",
            "-fno-omit-frame-pointer", "-fno-sanitize-recover=undefined", "-D__HIP_PLATFORM_AMD__",
            "-I/opt/rocm/include", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "block_list.cpp"), str(stub),
-           "-o", str(lib), "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"]
+           os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "block_list.cpp"),
+           os.path.join(CSRC, "plan.cpp"), str(stub), "-o", str(lib), "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
     env = dict(os.environ, LD_PRELOAD=f"{asan} {ubsan}", ASAN_OPTIONS="detect_leaks=0",
@@ -152,6 +165,14 @@ static void worker(int t) {
             MESH_ATTN_ERR_INVALID)
             ++bad;
         if (std::strcmp(mesh_attn_last_error(), "tile_fwd: part_len must be >= 1") != 0) ++bad;
+        mesh_attn_plan_costs pc = {1.0, 0.5, 1.0, 0.75, 0.375, 1};
+        mesh_attn_plan_step steps[256];
+        mesh_attn_block order[MESH_ATTN_MAX_BLOCKS];
+        int32_t ns = 0, no = 0;
+        if (mesh_attn_plan(R, C, R / 2, C / 2, 1, 1, &pc, steps, 256, &ns, order,
+                           MESH_ATTN_MAX_BLOCKS, &no) != MESH_ATTN_OK ||
+            ns < 1 || steps[ns - 1].end_s <= 0.0)
+            ++bad;
     }
 }
 
@@ -179,7 +200,8 @@ def test_host_code_under_tsan(tmp_path):
     cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=thread", "-D__HIP_PLATFORM_AMD__",
            "-I/opt/rocm/include", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "block_list.cpp"),
-           str(tmp_path / "stub.cpp"), str(tmp_path / "driver.cpp"), "-o", str(exe),
+           os.path.join(CSRC, "plan.cpp"), str(tmp_path / "stub.cpp"), str(tmp_path / "driver.cpp"),
+           "-o", str(exe),
            "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-pthread"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr

@@ -35,10 +35,15 @@
 //     reading 4-dim pieces of four key rows give every lane four keys of its
 //     own dim.
 //
-// Online softmax with a lazy shift: a row keeps the shift m it used so far
-// and only moves it (rescaling O and l) when a new score exceeds it by more
-// than 2^8 in base 2; otherwise probabilities up to 2^8 are accumulated as
-// they are.  The result is the same softmax, since O and l share the shift.
+// Online softmax with a checked shift: a row's exponentials are taken
+// against a shift that starts at the exact maximum of the row's first 32
+// keys.  O and l share the shift, so any shift gives the same softmax as
+// long as nothing overflows; instead of a row maximum per 32 keys, each
+// half's exponent sum is checked, and only when it exceeds 2^20 (or
+// overflowed) does the wave take the rescue path: the shift moves to the
+// half's exact row maximum, O and l are rescaled, and the half's
+// exponentials are taken again.  Probabilities below 2^20 are accumulated
+// as they are; fp32 and bf16 keep their relative precision at that scale.
 //
 // LDS layouts (row-major, 16-byte chunks swizzled so that reads are free of
 // bank conflicts; the DMA writes are contiguous per wave)
@@ -74,7 +79,7 @@ constexpr int NT = NW * 64;
 constexpr int kNBuf = 5;                    // LDS tiles in flight (5 x 32 KiB = all of LDS)
 constexpr int kTileBytes = BN * D * 2;      // 16 KiB per K or V tile
 constexpr int kBufBytes = 2 * kTileBytes;   // K then V
-constexpr float kShiftSlack = 8.0f;         // base-2 headroom before the shift moves
+constexpr float kHalfSumLimit = 1048576.0f;  // 2^20: a half's exponent sum above it moves the shift
 constexpr int kRsrcWord3 = 0x00020000;      // buffer resource flags for gfx9 (raw, 32-bit)
 constexpr int kDmaRegions = 2 * kTileBytes / 1024;       // 1 KiB DMA loads per tile
 constexpr int kDmaPerWave = (kDmaRegions + NW - 1) / NW;  // per wave (the last may idle)
@@ -210,31 +215,42 @@ __device__ __forceinline__ float row_max(const f32x16& s) {
     return dev::max_with_partner(mx);
 }
 
-// Moves the shift where a row's new maximum (scaled) outgrew it by the slack,
-// rescaling O and l.  Wave-uniform branch: rarely taken after the first half.
-__device__ __forceinline__ void update_shift(float m_cand, float& m, float& l, f32x16 (&o)[4]) {
-    const bool need = m_cand > m + kShiftSlack;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-        const float m_new = need ? m_cand : m;
-        const float alpha = need ? dev::fast_exp2(m - m_new) : 1.0f;
-        m = m_new;
-        l *= alpha;
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
-    }
-}
-
-// P = exp2(S*c - m) in bf16, laid out as the B operand of the PV MFMAs; l += sum P.
-__device__ __forceinline__ void softmax_half(const f32x16& s, float c2, float m, float& l, bf16x8 (&pb)[2]) {
-    const float shift = m == kNegInf ? 0.0f : m;
+// P = exp2(S*c - shift) in bf16, laid out as the B operand of the PV
+// MFMAs; returns this lane's sum of P over the half.
+__device__ __forceinline__ float softmax_half(const f32x16& s, float c2, float shift, bf16x8 (&pb)[2]) {
+    float h = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const float pv = dev::fast_exp2(__builtin_fmaf(s[i], c2, -shift));
-        l += pv;
+        h += pv;
         pb[i >> 3][i & 7] = static_cast<__bf16>(pv);
     }
+    return h;
+}
+
+// Rescue path (wave-uniform, rare): a half's exponent sum outgrew the limit.
+// The shift moves up to the half's exact row maximum (never down), O and l
+// are rescaled, and the half's probabilities are taken again.
+__device__ __forceinline__ void rescue_half(const f32x16& s, float c2, float& shift, float& l,
+                                                      f32x16 (&o)[4], bf16x8 (&pb)[2], float& h) {
+    const float cand = row_max(s) * c2;
+    const float next = cand > shift ? cand : shift;
+    const float alpha = dev::fast_exp2(shift - next);
+    shift = next;
+    l *= alpha;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+    h = softmax_half(s, c2, shift, pb);
+}
+
+// Checks a half's exponent sum and folds it into l.
+__device__ __forceinline__ void settle_half(const f32x16& s, float c2, float& shift, float& l, f32x16 (&o)[4],
+                                            bf16x8 (&pb)[2], float h) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(h <= kHalfSumLimit)) != 0, 0))
+        rescue_half(s, c2, shift, l, o, pb, h);
+    l += h;
 }
 
 __global__ __launch_bounds__(NT, 1) void tile_fwd_bf16_d128(const TileParams p) {
@@ -273,8 +289,8 @@ __global__ __launch_bounds__(NT, 1) void tile_fwd_bf16_d128(const TileParams p) 
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[t][i] = 0.0f;
-    float m = kNegInf;  // shift in use (scaled base-2 scores)
-    float l = 0.0f;     // exponent sum over this lane's keys
+    float shift = 0.0f;  // shift of the exponentials (scaled base-2 scores), uniform per row
+    float l = 0.0f;      // exponent sum over this lane's keys
 
     const int b_beg = p.sched.blk_off[w.q_slot];
     const int b_end = p.sched.blk_off[w.q_slot + 1];
@@ -338,28 +354,29 @@ __global__ __launch_bounds__(NT, 1) void tile_fwd_bf16_d128(const TileParams p) 
 
         f32x16 s = qk_half(ln, qf, lds, 0);
         if (needs_mask(dg, n0)) mask_half(s, n0, L, dg, u);
-        update_shift(row_max(s) * c2, m, l, o);
+        {
+            const float m0 = row_max(s) * c2;
+            shift = m0 == kNegInf ? 0.0f : m0;  // a row with no visible key yet keeps 0
+        }
 
         // One pipeline step from half H of the tile in `cur` to the next half
         // (half 1 of the same tile, or half 0 of the next tile in `nxt`).
         auto step = [&](auto h_tag, const LDS_AS unsigned char* cur, const LDS_AS unsigned char* nxt,
                         bool mask_next, bool diag_next, int key0_next) {
             constexpr int H = decltype(h_tag)::value;
-            // QK^T of the next half with the exponentials of this half, and
-            // the next half's row maximum, at a raised wave priority: the
-            // SIMD's arbiter then favours the wave whose dependent QK chain is
-            // waiting to issue over the other two waves' PV work (measured:
-            // ~2.5% faster than no priority).
+            // QK^T of the next half with the exponentials of this half at a
+            // raised wave priority: the SIMD's arbiter then favours the wave
+            // whose dependent QK chain is waiting to issue over the other two
+            // waves' PV work.
             __builtin_amdgcn_s_setprio(1);
             f32x16 s_next = qk_half(ln, qf, nxt, H ^ 1);
             bf16x8 pb[2];
-            softmax_half(s, c2, m, l, pb);
+            const float h = softmax_half(s, c2, shift, pb);
             if (mask_next) mask_half(s_next, key0_next, L, diag_next, u);
-            const float m_cand = row_max(s_next) * c2;
             __builtin_amdgcn_s_setprio(0);
+            settle_half(s, c2, shift, l, o, pb, h);
             // PV of this half.
             pv_half(ln, o, pb, cur, H);
-            update_shift(m_cand, m, l, o);
             s = s_next;
         };
 
@@ -390,11 +407,12 @@ __global__ __launch_bounds__(NT, 1) void tile_fwd_bf16_d128(const TileParams p) 
         }
         // Second half of the last tile.
         bf16x8 pb[2];
-        softmax_half(s, c2, m, l, pb);
+        const float h = softmax_half(s, c2, shift, pb);
+        settle_half(s, c2, shift, l, o, pb, h);
         pv_half(ln, o, pb, lds + buf * kBufBytes, 1);
     }
 
-    // Epilogue: O = O_acc / l, lse = ln(2) * (m + log2 l); empty rows -> (0, -inf).
+    // Epilogue: O = O_acc / l, lse = ln(2) * (shift + log2 l); empty rows -> (0, -inf).
     const float l_tot = dev::add_with_partner(l);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     if (u < L) {
@@ -409,7 +427,7 @@ __global__ __launch_bounds__(NT, 1) void tile_fwd_bf16_d128(const TileParams p) 
                 for (int j = 0; j < 4; ++j) ov[j] = static_cast<__bf16>(o[t][4 * ib + j] * inv);
                 *reinterpret_cast<bf16x4*>(op + 32 * t + 8 * ib + 4 * g) = ov;
             }
-        if (g == 0) p.lse[q_row] = l_tot > 0.0f ? (m + __log2f(l_tot)) * dev::kLn2 : kNegInf;
+        if (g == 0) p.lse[q_row] = l_tot > 0.0f ? (shift + __log2f(l_tot)) * dev::kLn2 : kNegInf;
     }
 }
 

@@ -419,6 +419,15 @@ __global__ __launch_bounds__(KT, 1) void tile_bwd_dkdv_bf16_d128(const BwdDkvPar
 #pragma unroll
         for (int c = 0; c < 8; ++c)
             vf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vr, r32 * kv_row_bytes + (16 * c + 8 * g) * 2, 0, 0));
+        // Wait for V here: left to its first use inside the loop, the wait
+        // counts the untracked stage DMA too and would stall every stage on
+        // the next stage's loads.
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            u32x4 t = __builtin_bit_cast(u32x4, vf[c]);
+            asm volatile("" : "+v"(t));
+            vf[c] = __builtin_bit_cast(bf16x8, t);
+        }
     }
 
     f32x16 dk[4], dv[4];
@@ -448,8 +457,12 @@ __global__ __launch_bounds__(KT, 1) void tile_bwd_dkdv_bf16_d128(const BwdDkvPar
     };
 
     // Issues the loads of item (e_, r0_, hh_) into stage st: Q and dO rows by
-    // DMA (rows at or past L read as zero), the row terms by wave 0 through
-    // registers (-lse/scale, -inf for rows that see nothing; -D).
+    // DMA (rows at or past L read as zero), and, on wave 0, the rows' lse and
+    // D into registers (one row per lane).  The row terms reach LDS through
+    // store_terms once the current stage's work is done, so that wave 0 does
+    // not wait for this stage's loads before its own matrix work.
+    float ls_in = kNegInf, dl_in = 0.0f;
+    int rr_in = 0;
     auto load_item = [&](int e_, int r0_, int hh_, int st) {
         const int s = kv_entry(p.sched, e_) >> 2;
         const int h = kv_head * G + hh_;
@@ -463,13 +476,22 @@ __global__ __launch_bounds__(KT, 1) void tile_bwd_dkdv_bf16_d128(const BwdDkvPar
             dma_1k(dst + reg * 1024, dma_gofs[i], reg < 16 ? qd : dd);
         }
         if (wave == 0) {
-            const int rr = r0_ + lane;
-            const size_t qi = (size_t)(s * L + min(rr, L - 1)) * p.heads_q + h;
-            const float ls = rr < L ? p.lse[qi] : kNegInf;
-            const float dl = rr < L ? p.delta[qi] : 0.0f;
+            // Unconditional loads of an in-range row (the last one for rows
+            // past L); store_terms decides what the row contributes.
+            rr_in = r0_ + lane;
+            const size_t qi = (size_t)(s * L + min(rr_in, L - 1)) * p.heads_q + h;
+            ls_in = p.lse[qi];
+            dl_in = p.delta[qi];
+        }
+    };
+    // Row terms of the loaded item into stage st: -lse/scale (-inf for rows
+    // that see nothing) and -D, one float per row (wave 0).
+    auto store_terms = [&](int st) {
+        if (wave == 0) {
             LDS_AS float* terms = reinterpret_cast<LDS_AS float*>(lds + kKTileBytes + st * kStageBytes + kTermOff);
-            terms[lane] = ls > kNegInf ? ls * neg_inv_scale : kNegInf;
-            terms[kRows + lane] = -dl;
+            const bool live = rr_in < L && ls_in > kNegInf;
+            terms[lane] = live ? ls_in * neg_inv_scale : kNegInf;
+            terms[kRows + lane] = live ? -dl_in : 0.0f;
         }
     };
     auto vmcnt0_barrier = [&]() {
@@ -479,7 +501,10 @@ __global__ __launch_bounds__(KT, 1) void tile_bwd_dkdv_bf16_d128(const BwdDkvPar
 
     const LDS_AS unsigned char* kw_tile = ktile + 32 * wave * kRowBytes;
     int st = 0;
-    if (e < e_end) load_item(e, r0, hh, 0);
+    if (e < e_end) {
+        load_item(e, r0, hh, 0);
+        store_terms(0);
+    }
     vmcnt0_barrier();  // K tile and stage 0
 
     while (e < e_end) {
@@ -538,6 +563,7 @@ __global__ __launch_bounds__(KT, 1) void tile_bwd_dkdv_bf16_d128(const BwdDkvPar
                     dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(to, qb, t, kk), dsb[kk], dk[t], 0, 0, 0);
                 }
         }
+        store_terms(st ^ 1);  // unused when this was the last item
         vmcnt0_barrier();  // the next stage has landed; this one is free
         st ^= 1;
         e = e1;

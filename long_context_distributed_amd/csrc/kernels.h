@@ -65,11 +65,15 @@ struct TileParams {
 
 static_assert(offsetof(TileParams, sched) % 4 == 0, "schedule must be dword aligned");
 
-// Waves per workgroup and query rows per wave of the tile kernels.
+// Waves per workgroup and query rows per wave of the tile kernels.  In the
+// float32 kernel all waves of a workgroup share one block of rows and split
+// its keys among themselves: kTileWavesF32 waves own rows (one), and
+// kTileKeySplitF32 waves run per workgroup.
 constexpr int kTileWavesBf16 = 12;
-constexpr int kTileWavesF32 = 4;
+constexpr int kTileWavesF32 = 1;
+constexpr int kTileKeySplitF32 = 4;
 constexpr int kWaveRowsBf16 = 32;
-constexpr int kWaveRowsF32 = 32;
+constexpr int kWaveRowsF32 = 16;
 
 // The same blocks seen from the KV side, for the key/value-gradient kernel:
 // for KV slot j the entries blk[blk_off[j] .. blk_off[j+1]) are

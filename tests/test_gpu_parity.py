@@ -32,6 +32,11 @@ SMALL = [
     ("f32", 64, (2, 2), (0, 0), False, False, 1, 1, 64),
     ("f32", 33, (2, 2), (1, 1), True, True, 2, 1, 64),
     ("f32", 40, (4, 2), (2, 1), True, True, 4, 2, 128),
+    ("f32", 150, (4, 4), (2, 1), True, True, 6, 2, 128),   # several key tiles per wave, ragged, G=3
+    ("f32", 200, (3, 2), (1, 0), True, False, 2, 2, 64),   # contiguous KV, two diagonal blocks
+    ("f32", 7, (2, 2), (1, 1), True, True, 3, 1, 64),      # fewer keys than waves
+    ("f32", 300, (2, 2), (1, 0), True, True, 2, 1, 64),    # causal, several 64-row blocks per diagonal
+    ("f32", 1000, (2, 2), (1, 0), False, True, 2, 1, 64),  # long non-causal rows
 ]
 
 
@@ -215,3 +220,18 @@ def test_running_pairwise_merge_one_kv_slot_at_a_time(R, C, r, c, L, hq, hkv):
     ref_o, ref_lse = oracle.tile_rows_ref(t["q"], t["k"], t["v"], t["q_parts"], t["kv_parts"],
                                           L, True, 1.0 / math.sqrt(128))
     compare(o_run, lse_run, ref_o, ref_lse, "bf16", what=f"running merge over {R} KV slots")
+
+
+@pytest.mark.parametrize("L,mesh,tile,hq,hkv,d", [(4096, (2, 2), (1, 0), 4, 2, 64),
+                                                  (2048, (4, 2), (2, 1), 8, 2, 128)])
+def test_f32_long_causal_partitions_sampled_rows(L, mesh, tile, hq, hkv, d):
+    """Float32 causal tiles with long partitions (thousands of keys per
+    diagonal block), checked on seeded sampled rows plus the edge rows of
+    every Q slot at the float32 bound."""
+    w = workloads.small("f32", L, mesh[0], mesh[1], tile[0], tile[1], True, True, hq, hkv, d)
+    say(f"[case] {w.name}")
+    t = run_tile(w)
+    rows = workloads.sample_rows(t["q"].shape[0], hq, hkv, L, n_sample=512, seed=4)
+    ref_o, ref_lse = oracle.tile_rows_ref(t["q"], t["k"], t["v"], t["q_parts"], t["kv_parts"], L, True,
+                                          1.0 / math.sqrt(d), rows=rows)
+    compare(t["o"], t["lse"], ref_o, ref_lse, "f32", rows=rows, what=w.name)

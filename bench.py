@@ -36,6 +36,13 @@ row were read.
 that a hardware-counter run can scale FETCH_SIZE / WRITE_SIZE by what they
 read for a copy of known size.
 
+--gemm-ceiling MS runs the vendor bf16 GEMM (torch.mm, 8192^3, contiguous
+operands) back to back for about MS milliseconds after the steps and reports
+its rate under "gemm_ceiling": a dense matrix-core load of the tile's
+duration, run at the clock the GPU holds under such a load, as a ceiling to
+read the tile kernel's fraction of the spec peak against.  It is a reference
+measurement, not part of the hot path.
+
 Prints one JSON line on stdout (everything else goes to stderr).
 """
 import argparse
@@ -479,6 +486,37 @@ def plan_leg(w, blocks, t_tile_ms):
     return res
 
 
+def gemm_ceiling(ms, dev):
+    """Vendor bf16 GEMM (8192 x 8192 x 8192) run back to back for ~ms
+    milliseconds; returns its rate and the duration measured with events."""
+    import torch
+    n = 8192
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    a = torch.randn((n, n), generator=gen, device=dev).to(torch.bfloat16).contiguous()
+    b = torch.randn((n, n), generator=gen, device=dev).to(torch.bfloat16).contiguous()
+    c = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    torch.mm(a, b, out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    torch.mm(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    reps = max(1, int(ms / max(e0.elapsed_time(e1), 1e-3)))
+    e0.record()
+    for _ in range(reps):
+        torch.mm(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1)
+    tflops = 2.0 * n ** 3 * reps / (t * 1e-3) / 1e12
+    log(f"[bench] gemm ceiling: {reps} x bf16 {n}^3 in {t:.1f} ms = {tflops:.1f} TFLOP/s "
+        f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of {PEAK_BF16_TFLOPS})")
+    return {"kernel": "torch.mm bf16 8192^3 (vendor GEMM)", "reps": reps, "ms": t,
+            "tflops": tflops, "frac_peak": tflops / PEAK_BF16_TFLOPS}
+
+
 def _others(spec):
     if spec == "none":
         return []
@@ -499,6 +537,7 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--others", default="all",
                     help="other workloads measured after the headline: none, all or a list")
+    ap.add_argument("--gemm-ceiling", type=float, default=0.0, metavar="MS")
     ap.add_argument("--others-steps", type=int, default=5)
     ap.add_argument("--others-cpu-budget", type=float, default=5.0)
     a = ap.parse_args()
@@ -547,6 +586,8 @@ def main():
     result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                         "compute_units": props.multi_processor_count,
                         "memory_gib": round(props.total_memory / 2 ** 30, 1)}
+    if a.gemm_ceiling > 0:
+        result["gemm_ceiling"] = gemm_ceiling(a.gemm_ceiling, dev)
     others = _others(a.others)
     if others:
         per = {}

@@ -79,10 +79,10 @@ bool valid_cost(double x) { return isfinite(x) && x >= 0.0; }
 
 }  // namespace
 
-extern "C" int mesh_attn_plan(int32_t mesh_rows, int32_t mesh_cols, int32_t row, int32_t col,
-                              int32_t causal, int32_t kv_rotate, const mesh_attn_plan_costs* costs,
-                              mesh_attn_plan_step* steps, int32_t step_capacity, int32_t* n_steps,
-                              mesh_attn_block* order, int32_t order_capacity, int32_t* n_order) {
+static int plan_impl(int32_t mesh_rows, int32_t mesh_cols, int32_t row, int32_t col, int32_t causal,
+                     int32_t kv_rotate, const mesh_attn_plan_costs* costs, mesh_attn_plan_step* steps,
+                     int32_t step_capacity, int32_t* n_steps, mesh_attn_block* order, int32_t order_capacity,
+                     int32_t* n_order) {
     using mesh_attn::fail;
     if (costs == nullptr) return fail(MESH_ATTN_ERR_INVALID, "plan: costs is NULL");
     if (n_steps == nullptr || n_order == nullptr)
@@ -259,4 +259,17 @@ extern "C" int mesh_attn_plan(int32_t mesh_rows, int32_t mesh_cols, int32_t row,
     std::copy(out_order.begin(), out_order.end(), order);
     mesh_attn::clear_error();
     return MESH_ATTN_OK;
+}
+
+extern "C" int mesh_attn_plan(int32_t mesh_rows, int32_t mesh_cols, int32_t row, int32_t col,
+                              int32_t causal, int32_t kv_rotate, const mesh_attn_plan_costs* costs,
+                              mesh_attn_plan_step* steps, int32_t step_capacity, int32_t* n_steps,
+                              mesh_attn_block* order, int32_t order_capacity, int32_t* n_order) {
+    // No exception crosses the C ABI (the only source is host memory exhaustion).
+    try {
+        return plan_impl(mesh_rows, mesh_cols, row, col, causal, kv_rotate, costs, steps, step_capacity,
+                         n_steps, order, order_capacity, n_order);
+    } catch (...) {
+        return mesh_attn::fail(MESH_ATTN_ERR_INVALID, "plan: out of host memory");
+    }
 }

@@ -43,6 +43,13 @@ duration, run at the clock the GPU holds under such a load, as a ceiling to
 read the tile kernel's fraction of the spec peak against.  It is a reference
 measurement, not part of the hot path.
 
+--sdpa-reference times the vendor attention (torch scaled_dot_product_attention
+with its flash backend forced) on the headline tile's block shapes, one FULL
+block without a mask and one DIAG block with the causal mask (K/V heads
+repeated to the query heads), and reports under "sdpa_reference" the time a
+tile of the same block counts would take, n_full * t_full + n_diag * t_diag,
+with the rate on the tile's algorithmic flops.  Also a reference measurement.
+
 Prints one JSON line on stdout (everything else goes to stderr).
 """
 import argparse
@@ -517,6 +524,54 @@ def gemm_ceiling(ms, dev):
             "tflops": tflops, "frac_peak": tflops / PEAK_BF16_TFLOPS}
 
 
+def sdpa_reference(wid, dev, reps=5):
+    """Vendor attention on one FULL and one DIAG block of the workload (see
+    --sdpa-reference); a dict with the block times and the tile-equivalent
+    rate, or the reason it could not run."""
+    import torch
+    import long_context_distributed_amd as mat
+    import workloads
+
+    w = workloads.WORKLOADS[wid]
+    if w.dtype != "bf16":
+        return {"error": "the flash backend takes bf16 / fp16 only"}
+    blocks = mat.block_list(w.mesh_rows, w.mesh_cols, w.tile_row, w.tile_col, w.causal, w.kv_rotate)
+    n_full = sum(1 for b in blocks if b[4] == mat.FULL)
+    n_diag = sum(1 for b in blocks if b[4] == mat.DIAG)
+    L, hq, d = w.part_len, w.heads_q, w.head_dim
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    q, k, v = (torch.randn((1, hq, L, d), generator=gen, device=dev).to(torch.bfloat16).contiguous()
+               for _ in range(3))
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+    except ImportError as e:
+        return {"error": f"torch.nn.attention unavailable: {e}"}
+    res = {"kernel": "torch scaled_dot_product_attention (flash backend)",
+           "shape": f"1 x {hq} heads x {L} x {d}, bf16", "n_full": n_full, "n_diag": n_diag}
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            for causal, key in ((False, "full_block_ms"), (True, "diag_block_ms")):
+                torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal)
+                e1.record()
+                torch.cuda.synchronize()
+                res[key] = e0.elapsed_time(e1) / reps
+    except RuntimeError as e:
+        return {"error": f"flash backend unavailable: {str(e)[:200]}"}
+    t = n_full * res["full_block_ms"] + n_diag * res["diag_block_ms"]
+    flops = tile_flops(blocks, L, hq, d)
+    res.update({"tile_equiv_ms": t, "tflops": flops / (t * 1e-3) / 1e12})
+    res["frac_peak"] = res["tflops"] / PEAK_BF16_TFLOPS
+    log(f"[bench] sdpa reference: FULL {res['full_block_ms']:.3f} ms, DIAG {res['diag_block_ms']:.3f} ms, "
+        f"tile of {n_full}F/{n_diag}D {t:.1f} ms = {res['tflops']:.1f} TFLOP/s")
+    return res
+
+
 def _others(spec):
     if spec == "none":
         return []
@@ -538,6 +593,7 @@ def main():
     ap.add_argument("--others", default="all",
                     help="other workloads measured after the headline: none, all or a list")
     ap.add_argument("--gemm-ceiling", type=float, default=0.0, metavar="MS")
+    ap.add_argument("--sdpa-reference", action="store_true")
     ap.add_argument("--others-steps", type=int, default=5)
     ap.add_argument("--others-cpu-budget", type=float, default=5.0)
     a = ap.parse_args()
@@ -588,6 +644,8 @@ def main():
                         "memory_gib": round(props.total_memory / 2 ** 30, 1)}
     if a.gemm_ceiling > 0:
         result["gemm_ceiling"] = gemm_ceiling(a.gemm_ceiling, dev)
+    if a.sdpa_reference:
+        result["sdpa_reference"] = sdpa_reference(a.workload, dev)
     others = _others(a.others)
     if others:
         per = {}

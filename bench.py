@@ -36,19 +36,23 @@ row were read.
 that a hardware-counter run can scale FETCH_SIZE / WRITE_SIZE by what they
 read for a copy of known size.
 
---gemm-ceiling MS runs the vendor bf16 GEMM (torch.mm, 8192^3, contiguous
-operands) back to back for about MS milliseconds after the steps and reports
+--gemm-ceiling MS (default 130; 0 skips it) runs the vendor bf16 GEMM
+(torch.mm, 8192^3, contiguous operands) back to back for about MS
+milliseconds after the headline's steps and reports
 its rate under "gemm_ceiling": a dense matrix-core load of the tile's
 duration, run at the clock the GPU holds under such a load, as a ceiling to
 read the tile kernel's fraction of the spec peak against.  It is a reference
 measurement, not part of the hot path.
 
---sdpa-reference times the vendor attention (torch scaled_dot_product_attention
-with its flash backend forced) on the headline tile's block shapes, one FULL
+The vendor attention reference (on by default; --no-sdpa-reference skips it)
+times torch scaled_dot_product_attention with its flash backend forced on the
+headline tile's block shapes, one FULL
 block without a mask and one DIAG block with the causal mask (K/V heads
 repeated to the query heads), and reports under "sdpa_reference" the time a
 tile of the same block counts would take, n_full * t_full + n_diag * t_diag,
-with the rate on the tile's algorithmic flops.  Also a reference measurement.
+with the rate on the tile's algorithmic flops and the tile kernel's speedup
+over it.  Also a reference measurement.  Either reference that fails is
+reported with its error instead of its figures.
 
 Prints one JSON line on stdout (everything else goes to stderr).
 """
@@ -315,10 +319,14 @@ def _peer_partials(w, mat, q_parts, n_tok, rows, d, dtype, dev):
     return o_parts, l_parts, own
 
 
-def measure_workload(wid, steps, warmup, backward_steps, cpu_budget, copy_calibration, dev):
+def measure_workload(wid, steps, warmup, backward_steps, cpu_budget, copy_calibration, dev,
+                     after_forward=None):
     """Times whole steps (block list + tile forward + merge) of one workload,
     with per-kernel HIP events on the launch stream, then the backward, then
-    the oracle on host cores.  Returns (result dict, step ms)."""
+    the oracle on host cores.  after_forward(result) -> dict, if given, runs
+    right after the forward steps (the GPU still at the clock it holds under
+    that load) and its entries join the result.  Returns (result dict, step
+    ms)."""
     import torch
     import long_context_distributed_amd as mat
     import workloads
@@ -412,6 +420,8 @@ def measure_workload(wid, steps, warmup, backward_steps, cpu_budget, copy_calibr
                       "live_partial_rows": live, "partial_rows": n_parts * rows,
                       "traffic": measured_traffic("lse_merge_kernel", wid)},
     }
+    if after_forward is not None:
+        res.update(after_forward(res))
     # Row a1 (host): the block list of this tile, library call against the oracle's brute force.
     t0 = time.perf_counter()
     for _ in range(1000):
@@ -592,8 +602,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--others", default="all",
                     help="other workloads measured after the headline: none, all or a list")
-    ap.add_argument("--gemm-ceiling", type=float, default=0.0, metavar="MS")
-    ap.add_argument("--sdpa-reference", action="store_true")
+    ap.add_argument("--gemm-ceiling", type=float, default=130.0, metavar="MS")
+    ap.add_argument("--sdpa-reference", dest="sdpa_reference", action="store_true", default=True)
+    ap.add_argument("--no-sdpa-reference", dest="sdpa_reference", action="store_false")
     ap.add_argument("--others-steps", type=int, default=5)
     ap.add_argument("--others-cpu-budget", type=float, default=5.0)
     a = ap.parse_args()
@@ -610,8 +621,28 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     cpu_budget = 0.0 if a.no_cpu_baseline else a.cpu_budget
+
+    def references(res):
+        """The vendor GEMM and vendor attention references, run right after
+        the headline's forward steps."""
+        out = {}
+        if a.gemm_ceiling > 0:
+            try:
+                out["gemm_ceiling"] = gemm_ceiling(a.gemm_ceiling, dev)
+            except RuntimeError as e:
+                out["gemm_ceiling"] = {"error": str(e)[:200]}
+        if a.sdpa_reference:
+            try:
+                ref = sdpa_reference(a.workload, dev)
+            except RuntimeError as e:
+                ref = {"error": str(e)[:200]}
+            if "tile_equiv_ms" in ref:
+                ref["tile_fwd_speedup"] = ref["tile_equiv_ms"] / res["tile_fwd"]["ms"]
+            out["sdpa_reference"] = ref
+        return out
+
     head, ms_step = measure_workload(a.workload, a.steps, a.warmup, a.backward_steps, cpu_budget,
-                                     a.copy_calibration, dev)
+                                     a.copy_calibration, dev, after_forward=references)
     tf = head["tile_fwd"]
     result = {
         "metric": METRIC,
@@ -642,16 +673,16 @@ def main():
     result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                         "compute_units": props.multi_processor_count,
                         "memory_gib": round(props.total_memory / 2 ** 30, 1)}
-    if a.gemm_ceiling > 0:
-        result["gemm_ceiling"] = gemm_ceiling(a.gemm_ceiling, dev)
-    if a.sdpa_reference:
-        result["sdpa_reference"] = sdpa_reference(a.workload, dev)
+    for key in ("gemm_ceiling", "sdpa_reference"):
+        if key in head:
+            result[key] = head[key]
     others = _others(a.others)
     if others:
         per = {}
         for wid in others:
             if wid == a.workload:
-                per[str(wid)] = {k_: v_ for k_, v_ in head.items()}
+                per[str(wid)] = {k_: v_ for k_, v_ in head.items()
+                                 if k_ not in ("gemm_ceiling", "sdpa_reference")}
                 continue
             res, _ = measure_workload(wid, a.others_steps, 1, 2 if a.backward_steps > 0 else 0,
                                       0.0 if a.no_cpu_baseline else a.others_cpu_budget, 0, dev)

@@ -79,7 +79,6 @@ def load():
             "(there is no CPU fallback)")
     lib = ctypes.CDLL(LIB_PATH)
     i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
-    fp = ctypes.POINTER(ctypes.c_float)
     lib.mesh_attn_block_list.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(Block), i32,
                                          ctypes.POINTER(i32)]
     lib.mesh_attn_block_list.restype = ctypes.c_int
@@ -101,6 +100,5 @@ def load():
     lib.mesh_attn_last_error.restype = ctypes.c_char_p
     lib.mesh_attn_version.argtypes = []
     lib.mesh_attn_version.restype = i32
-    del fp
     _LIB = lib
     return lib

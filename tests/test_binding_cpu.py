@@ -52,3 +52,14 @@ def test_outputs_must_not_overlap():
     with pytest.raises(ValueError, match="overlap"):
         mat._no_overlap([a, c], [b])          # two outputs over each other
     mat._no_overlap([base[:0]], [a])          # empty output
+
+
+def test_missing_library_raises_instead_of_falling_back(monkeypatch, tmp_path):
+    """Without the built library the binding raises; nothing computes on the host."""
+    from long_context_distributed_amd import _lib
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libmeshattn.so"))
+    monkeypatch.setattr(_lib, "_LIB", None)
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        _lib.load()
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        mat.block_list(2, 2, 0, 0, True, True)

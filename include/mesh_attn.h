@@ -285,7 +285,8 @@ typedef struct {
  * written): a size query.  MESH_ATTN_ERR_INVALID: NULL costs, n_steps or
  * n_order; a cost not finite or negative; delay not 0 or 1; mesh_rows > 64
  * or mesh_cols > 64 (the tile limits); anything mesh_attn_block_list
- * rejects.
+ * rejects; host memory exhausted while planning (the last-error text says
+ * so).  No C++ exception leaves the call.
  */
 MESH_ATTN_API int mesh_attn_plan(int32_t mesh_rows, int32_t mesh_cols, int32_t row, int32_t col,
                    int32_t causal, int32_t kv_rotate, const mesh_attn_plan_costs *costs,

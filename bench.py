@@ -610,7 +610,7 @@ def main():
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's tile only: the hot path is one GPU's share of the "
-              "mesh and this build has no multi-GPU path; run it with --gpus 1", file=sys.stderr)
+              "mesh and the library has no multi-GPU path; run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
